@@ -1,0 +1,274 @@
+#!/usr/bin/env python3
+"""Benchmark: causal-attention TFLOP/s of one context-parallel rank's share on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one pass of the whole hot path over one batch of synthetic input already resident
+in HBM.  For the default workload (ring_share_256k: S=262144, C=8 zigzag, rank 3, 32 query /
+8 KV heads, D=128, bf16) that is: the zigzag positions of every owner, then for each of the
+8 ring steps one block attention of the rank's 32768 local queries against the owner's
+32768-token K/V shard, folded into the accumulator by the LSE merge (7 merges).
+
+The value is whole-job throughput in TFLOP/s counting unmasked FLOPs only: 4*D FLOPs per
+visible (query, key) pair and query head (two matrix products; softmax not counted).
+The line also carries the roofline of the dominant kernel (block attention, measured with
+HIP events around each of its launches inside the timed steps) and the CPU oracle timed on
+a bounded sample of the same workload (``cpu_baseline``).
+
+One GPU only: --gpus above 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+METRIC = "causal attn TFLOP/s per rank share (unmasked FLOPs) + % of bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X published dense bf16 matrix peak
+PEAK_FP32_TFLOPS = 157.3    # MI355X published fp32 vector peak
+PEAK_HBM_GBS = 8000.0       # MI355X published HBM3E bandwidth
+
+
+def parse_args(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="ring_share_256k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle sample")
+    return ap.parse_args(argv)
+
+
+class Plan:
+    """Buffers and the launch sequence of one step of a workload."""
+
+    def __init__(self, w, dev):
+        import torch
+        import context_causal_attention_amd as cp
+        from context_causal_attention_amd import synthetic
+
+        self.w, self.dev, self.cp, self.torch = w, dev, cp, torch
+        td = {"bf16": torch.bfloat16, "fp32": torch.float32}[w.dtype]
+        kw = dict(batch=w.batch, chunk_len=w.chunk_len, head_dim=w.head_dim, dtype=td)
+        C = w.cp_size
+        self.kind = w.kind
+        self.attn_flops = []   # FLOPs of each block attention launch of a step, in order
+        if w.kind == "ring_share":
+            r = w.rank
+            self.q = synthetic.chunks("q", [r, 2 * C - 1 - r], heads=w.heads_q, **kw).to(dev)
+            self.k = [synthetic.chunks("k", [o, 2 * C - 1 - o], heads=w.heads_kv, **kw).to(dev) for o in range(C)]
+            self.v = [synthetic.chunks("v", [o, 2 * C - 1 - o], heads=w.heads_kv, **kw).to(dev) for o in range(C)]
+            self.pos = [torch.empty(w.local_len, dtype=torch.int64, device=dev) for _ in range(C)]
+            self.out = torch.empty((w.batch, w.local_len, w.heads_q, w.head_dim), dtype=torch.float32, device=dev)
+            self.lse = torch.empty((w.batch, w.heads_q, w.local_len), dtype=torch.float32, device=dev)
+            self.tout = torch.empty_like(self.out)
+            self.tlse = torch.empty_like(self.lse)
+            t = w.chunk_len
+            for step in range(C):
+                owner = (r - step) % C
+                pairs = 2 * t * t + t if owner == r else 2 * t * t
+                self.attn_flops.append(4.0 * w.batch * w.heads_q * w.head_dim * pairs)
+            self.merge_bytes = (3 * self.out.numel() * 4 + 3 * self.lse.numel() * 4)
+            self.n_merge = C - 1
+        elif w.kind == "allgather":
+            gather = [c for rr in range(C) for c in (rr, 2 * C - 1 - rr)]
+            self.kg = synthetic.chunks("k", gather, heads=w.heads_kv, **kw).to(dev)
+            self.vg = synthetic.chunks("v", gather, heads=w.heads_kv, **kw).to(dev)
+            self.kseq = torch.empty_like(self.kg)
+            self.vseq = torch.empty_like(self.vg)
+            self.qs = [synthetic.chunks("q", [rr, 2 * C - 1 - rr], heads=w.heads_q, **kw).to(dev) for rr in range(C)]
+            self.pos = [torch.empty(w.local_len, dtype=torch.int64, device=dev) for _ in range(C)]
+            self.gpos = torch.arange(w.seq_len, device=dev)
+            self.out = torch.empty((w.batch, w.local_len, w.heads_q, w.head_dim), dtype=torch.float32, device=dev)
+            self.lse = torch.empty((w.batch, w.heads_q, w.local_len), dtype=torch.float32, device=dev)
+            t = w.chunk_len
+            for rr in range(C):
+                pairs = 2 * C * t * t + t
+                self.attn_flops.append(4.0 * w.batch * w.heads_q * w.head_dim * pairs)
+            self.reorder_bytes = 2 * 2 * self.kg.numel() * self.kg.element_size()
+        elif w.kind == "ulysses":
+            s, g = w.local_len, w.group
+            stack = lambda x: x.reshape(w.batch, C, s, *x.shape[2:]).transpose(0, 1).contiguous()
+            ids = range(2 * C)
+            self.qst = stack(synthetic.chunks("q", ids, heads=w.heads_q, **kw)).to(dev)
+            self.kst = stack(synthetic.chunks("k", ids, heads=w.heads_kv, **kw)).to(dev)
+            self.vst = stack(synthetic.chunks("v", ids, heads=w.heads_kv, **kw)).to(dev)
+            hq, hk = w.heads_q // C, w.heads_kv // C
+            self.qg = torch.empty((w.batch, w.seq_len, hq, w.head_dim), dtype=td, device=dev)
+            self.kgp = torch.empty((w.batch, w.seq_len, hk, w.head_dim), dtype=td, device=dev)
+            self.vgp = torch.empty_like(self.kgp)
+            self.gpos = torch.arange(w.seq_len, device=dev)
+            self.og = torch.empty((w.batch, w.seq_len, hq, w.head_dim), dtype=torch.float32, device=dev)
+            self.lg = torch.empty((w.batch, hq, w.seq_len), dtype=torch.float32, device=dev)
+            self.ost = torch.zeros((C, w.batch, s, w.heads_q, w.head_dim), dtype=torch.float32, device=dev)
+            S = w.seq_len
+            self.attn_flops.append(4.0 * w.batch * hq * w.head_dim * (S * (S + 1) // 2))
+            el = self.qst.element_size()
+            self.permute_bytes = 2 * (self.qg.numel() + 2 * self.kgp.numel()) * el + 2 * self.og.numel() * 4
+        else:
+            raise ValueError(w.kind)
+        self.flops = sum(self.attn_flops)
+
+    def step(self, ev=None):
+        """Launch one step on the current stream.  ev: list to which (start, end) event
+        pairs around each block attention launch are appended."""
+        cp, torch, w = self.cp, self.torch, self.w
+        C = w.cp_size
+
+        def attn(*a, **k):
+            if ev is not None:
+                s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                s.record()
+                cp.block_fwd(*a, **k)
+                e.record()
+                ev.append((s, e))
+            else:
+                cp.block_fwd(*a, **k)
+
+        if self.kind == "ring_share":
+            r = w.rank
+            for o in range(C):
+                cp.zigzag_index(w.seq_len, C, o, out=self.pos[o])
+            for step in range(C):
+                owner = (r - step) % C
+                if step == 0:
+                    attn(self.q, self.k[owner], self.v[owner], self.pos[r], self.pos[owner], w.scale, self.out, self.lse)
+                else:
+                    attn(self.q, self.k[owner], self.v[owner], self.pos[r], self.pos[owner], w.scale, self.tout, self.tlse)
+                    cp.lse_merge(self.out, self.lse, self.tout, self.tlse)
+        elif self.kind == "allgather":
+            cp.reorder_gathered(self.kg, C, cp.RANK_TO_SEQ, out=self.kseq)
+            cp.reorder_gathered(self.vg, C, cp.RANK_TO_SEQ, out=self.vseq)
+            for rr in range(C):
+                cp.zigzag_index(w.seq_len, C, rr, out=self.pos[rr])
+                attn(self.qs[rr], self.kseq, self.vseq, self.pos[rr], self.gpos, w.scale, self.out, self.lse)
+        else:
+            g = w.group
+            cp.ulysses_seq_to_heads(self.qst, g, out=self.qg)
+            cp.ulysses_seq_to_heads(self.kst, g, out=self.kgp)
+            cp.ulysses_seq_to_heads(self.vst, g, out=self.vgp)
+            attn(self.qg, self.kgp, self.vgp, self.gpos, self.gpos, w.scale, self.og, self.lg)
+            cp.ulysses_heads_to_seq(self.og, g, self.ost)
+
+
+def cpu_baseline(w, budget_s: float):
+    """The CPU oracle (as it stands) on a bounded sample of the same workload: direct causal
+    attention of a seeded sample of the share's query rows, all heads, fp64."""
+    import numpy as np
+    import oracle
+    from context_causal_attention_amd import synthetic
+    import torch
+
+    td = {"bf16": torch.bfloat16, "fp32": torch.float32}[w.dtype]
+    kw = dict(batch=w.batch, chunk_len=w.chunk_len, head_dim=w.head_dim, dtype=td)
+    C, S = w.cp_size, w.seq_len
+    if w.kind == "ulysses":
+        hq, hk = w.heads_q // C, w.heads_kv // C
+        g = w.group
+        ids = list(range(2 * C))
+        q = synthetic.chunks("q", ids, heads=w.heads_q, **kw)[:, :, g * hq:(g + 1) * hq].float().numpy()
+        k = synthetic.chunks("k", ids, heads=w.heads_kv, **kw)[:, :, g * hk:(g + 1) * hk].float().numpy()
+        v = synthetic.chunks("v", ids, heads=w.heads_kv, **kw)[:, :, g * hk:(g + 1) * hk].float().numpy()
+        qpos = np.arange(S, dtype=np.int64)
+        heads = hq
+    else:
+        r = w.rank if w.rank is not None else C - 1
+        q = synthetic.chunks("q", [r, 2 * C - 1 - r], heads=w.heads_q, **kw).float().numpy()
+        k = synthetic.chunks("k", range(2 * C), heads=w.heads_kv, **kw).float().numpy()
+        v = synthetic.chunks("v", range(2 * C), heads=w.heads_kv, **kw).float().numpy()
+        qpos = oracle.zigzag_positions(S, C, r)
+        heads = w.heads_q
+    kvpos = np.arange(S, dtype=np.int64)
+    threads = oracle.default_threads()
+    rng = np.random.default_rng(0)
+    n_all = q.shape[1]
+
+    def run(n):
+        rows = np.sort(rng.choice(n_all, size=n, replace=False)).astype(np.int64)
+        pairs = int(np.searchsorted(kvpos, qpos[rows], side="right").sum()) * w.batch * heads
+        t0 = time.perf_counter()
+        oracle.attention_rows(q, k, v, qpos, kvpos, w.scale, rows=rows, nthreads=threads)
+        return pairs, time.perf_counter() - t0
+
+    pairs, dt = run(max(1, threads))                # calibration
+    n = int(max(1, min(n_all, threads * budget_s / max(dt, 1e-3))))
+    pairs, dt = run(n)
+    flops = 4.0 * w.head_dim * pairs
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} of {n_all} local query rows (seeded), all {heads} query heads, "
+                      f"{pairs} visible pairs, fp64, {dt:.1f} s"}
+
+
+def main(argv=None) -> int:
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(the rank share runs all ring steps on one device).", file=sys.stderr)
+        return 2
+    import torch
+    from context_causal_attention_amd.workloads import WORKLOADS
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    plan = Plan(w, dev)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        plan.step()
+    torch.cuda.synchronize()
+    ev = []
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_start.record()
+    for _ in range(args.steps):
+        plan.step(ev)
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+    value = plan.flops / (ms_step * 1e-3) / 1e12
+    attn_ms = [s.elapsed_time(e) for s, e in ev]
+    attn_flops = plan.attn_flops * args.steps
+    achieved = sum(attn_flops) / (sum(attn_ms) * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded iid N(0,1), per-chunk generators)",
+        "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seq_len, "cp_size": w.cp_size,
+                   "rank": w.rank, "group": w.group, "heads_q": w.heads_q, "heads_kv": w.heads_kv,
+                   "head_dim": w.head_dim, "unmasked_flops_per_step": plan.flops},
+        "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "kernel": "block_fwd_bf16_kernel" if w.dtype == "bf16" else "block_fwd_f32_kernel",
+                     "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "avg_launch_ms": round(sum(attn_ms) / len(attn_ms), 4), "launches": len(attn_ms)},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

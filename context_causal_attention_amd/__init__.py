@@ -1,0 +1,24 @@
+"""MI355X-native rank-share causal attention for context parallelism.
+
+One context-parallel rank's share of causal attention, computed blockwise on one GPU with
+hand-written gfx950 HIP kernels behind a C ABI (include/cpattn.h, libcpattn.so), plus the
+layout companions of the all-gather and Ulysses variants.  This package is the thin
+Python binding; build the library with ``python -m context_causal_attention_amd.build``.
+"""
+from ._binding import (  # noqa: F401
+    HEADS_TO_SEQ,
+    RANK_TO_SEQ,
+    SEQ_TO_HEADS,
+    SEQ_TO_RANK,
+    CpattnError,
+    block_fwd,
+    header_entry_points,
+    library_path,
+    load_library,
+    lse_merge,
+    reorder_gathered,
+    ring_share_fwd,
+    ulysses_heads_to_seq,
+    ulysses_seq_to_heads,
+    zigzag_index,
+)

@@ -1,0 +1,225 @@
+"""ctypes binding of libcpattn.so: argument marshalling only.
+
+Every function checks devices, dtypes, shapes and contiguity, passes raw device pointers
+and the current HIP stream to the C ABI (include/cpattn.h), and raises CpattnError on a
+non-zero status.  PyTorch supplies device memory and streams; all arithmetic happens in
+the library's kernels.  There is no fallback: without the built library every call fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import re
+from pathlib import Path
+
+import torch
+
+_PKG = Path(__file__).resolve().parent
+LIB_PATH = _PKG / "libcpattn.so"
+HEADER = _PKG.parent / "include" / "cpattn.h"
+
+CPATTN_F32, CPATTN_BF16 = 0, 1
+RANK_TO_SEQ, SEQ_TO_RANK = 0, 1
+SEQ_TO_HEADS, HEADS_TO_SEQ = 0, 1
+STATUS = {0: "CPATTN_OK", 1: "CPATTN_ERR_INVALID_ARG", 2: "CPATTN_ERR_SHAPE",
+          3: "CPATTN_ERR_UNSUPPORTED", 4: "CPATTN_ERR_HIP"}
+
+_lib = None
+
+
+class CpattnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def library_path() -> Path:
+    return LIB_PATH
+
+
+def load_library():
+    """Load libcpattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not LIB_PATH.exists():
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m context_causal_attention_amd.build`")
+    L = ctypes.CDLL(str(LIB_PATH))
+    P, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    L.cpattn_status_string.argtypes = [ctypes.c_int]
+    L.cpattn_status_string.restype = ctypes.c_char_p
+    L.cpattn_last_error.argtypes = []
+    L.cpattn_last_error.restype = ctypes.c_char_p
+    L.cpattn_abi_version.argtypes = []
+    L.cpattn_abi_version.restype = i32
+    L.cpattn_zigzag_index.argtypes = [i64, i32, i32, P, P]
+    L.cpattn_block_fwd.argtypes = [P, P, P, ctypes.c_int, i32, i64, i64, i32, i32, i32, P, P, f32, P, P, P]
+    L.cpattn_lse_merge.argtypes = [P, P, P, P, i32, i64, i32, i32, P]
+    L.cpattn_reorder_gathered.argtypes = [P, P, i32, i64, i64, i32, ctypes.c_int, P]
+    L.cpattn_ulysses_permute.argtypes = [P, P, i32, i32, i64, i32, i32, i32, i32, ctypes.c_int, P]
+    for name in ("cpattn_zigzag_index", "cpattn_block_fwd", "cpattn_lse_merge",
+                 "cpattn_reorder_gathered", "cpattn_ulysses_permute"):
+        getattr(L, name).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def header_entry_points() -> list[str]:
+    """Names of the functions declared in include/cpattn.h."""
+    text = HEADER.read_text()
+    return sorted(set(re.findall(r"\b(cpattn_[a-z0-9_]+)\s*\(", text)))
+
+
+def _check(status: int):
+    if status != 0:
+        msg = load_library().cpattn_last_error().decode(errors="replace")
+        raise CpattnError(status, msg)
+
+
+def _ptr(t: torch.Tensor | None):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+
+
+def zigzag_index(seq_len: int, cp_size: int, rank: int, out: torch.Tensor | None = None,
+                 device=None) -> torch.Tensor:
+    """Global positions of rank ``rank``'s local tokens (int64 [seq_len / cp_size])."""
+    L = load_library()
+    if out is None:
+        out = torch.empty(seq_len // max(cp_size, 1), dtype=torch.int64,
+                          device=device if device is not None else torch.device("cuda"))
+    _need(out, "out", torch.int64)
+    _check(L.cpattn_zigzag_index(seq_len, cp_size, rank, _ptr(out), _stream(out.device)))
+    return out
+
+
+def block_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_pos: torch.Tensor,
+              kv_pos: torch.Tensor, scale: float, out: torch.Tensor | None = None,
+              lse: torch.Tensor | None = None):
+    """One block of causal attention on global positions.
+
+    q [B, Sq, Hq, D]; k, v [B, Skv, Hkv, D] (both bf16 or both fp32); positions int64.
+    Returns (out fp32 [B, Sq, Hq, D], lse fp32 [B, Hq, Sq]).
+    """
+    L = load_library()
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("q must be bf16 or fp32")
+    B, Sq, Hq, D = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    _need(q, "q")
+    _need(k, "k", q.dtype, (B, Skv, Hkv, D))
+    _need(v, "v", q.dtype, (B, Skv, Hkv, D))
+    _need(q_pos, "q_pos", torch.int64, (Sq,))
+    _need(kv_pos, "kv_pos", torch.int64, (Skv,))
+    if out is None:
+        out = torch.empty((B, Sq, Hq, D), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, (B, Sq, Hq, D))
+    _need(lse, "lse", torch.float32, (B, Hq, Sq))
+    dt = CPATTN_BF16 if q.dtype == torch.bfloat16 else CPATTN_F32
+    _check(L.cpattn_block_fwd(_ptr(q), _ptr(k), _ptr(v), dt, B, Sq, Skv, Hq, Hkv, D, _ptr(q_pos),
+                              _ptr(kv_pos), float(scale), _ptr(out), _ptr(lse), _stream(q.device)))
+    return out, lse
+
+
+def lse_merge(out: torch.Tensor, lse: torch.Tensor, out_tile: torch.Tensor, lse_tile: torch.Tensor):
+    """Fold (out_tile, lse_tile) into (out, lse) in place; returns (out, lse)."""
+    L = load_library()
+    B, S, H, D = out.shape
+    _need(out, "out", torch.float32)
+    _need(lse, "lse", torch.float32, (B, H, S))
+    _need(out_tile, "out_tile", torch.float32, (B, S, H, D))
+    _need(lse_tile, "lse_tile", torch.float32, (B, H, S))
+    _check(L.cpattn_lse_merge(_ptr(out), _ptr(lse), _ptr(out_tile), _ptr(lse_tile), B, S, H, D,
+                              _stream(out.device)))
+    return out, lse
+
+
+def reorder_gathered(x: torch.Tensor, cp_size: int, direction: int = RANK_TO_SEQ,
+                     out: torch.Tensor | None = None) -> torch.Tensor:
+    """Chunk reorder of x [B, S, ...] between all-gather rank order and sequence order."""
+    L = load_library()
+    _need(x, "x")
+    if out is None:
+        out = torch.empty_like(x)
+    _need(out, "out", x.dtype, tuple(x.shape))
+    B, S = x.shape[0], x.shape[1]
+    row_bytes = x.numel() * x.element_size() // max(B * S, 1)
+    _check(L.cpattn_reorder_gathered(_ptr(x), _ptr(out), B, S, row_bytes, cp_size, direction,
+                                     _stream(x.device)))
+    return out
+
+
+def ulysses_seq_to_heads(stacked: torch.Tensor, group: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Stacked rank shards [C, B, S/C, H, D] -> head group ``group``'s [B, S, H/C, D]."""
+    L = load_library()
+    _need(stacked, "stacked")
+    C, B, s, H, D = stacked.shape
+    if out is None:
+        out = torch.empty((B, s * C, H // C, D), dtype=stacked.dtype, device=stacked.device)
+    _need(out, "out", stacked.dtype, (B, s * C, H // C, D))
+    _check(L.cpattn_ulysses_permute(_ptr(stacked), _ptr(out), stacked.element_size(), B, s * C, H, D,
+                                    C, group, SEQ_TO_HEADS, _stream(stacked.device)))
+    return out
+
+
+def ulysses_heads_to_seq(grouped: torch.Tensor, group: int, out: torch.Tensor) -> torch.Tensor:
+    """Head group ``group``'s [B, S, H/C, D] -> its heads of stacked out [C, B, S/C, H, D]."""
+    L = load_library()
+    _need(grouped, "grouped")
+    _need(out, "out", grouped.dtype)
+    C, B, s, H, D = out.shape
+    if tuple(grouped.shape) != (B, s * C, H // C, D):
+        raise ValueError(f"grouped must have shape {(B, s * C, H // C, D)}")
+    _check(L.cpattn_ulysses_permute(_ptr(grouped), _ptr(out), grouped.element_size(), B, s * C, H, D,
+                                    C, group, HEADS_TO_SEQ, _stream(grouped.device)))
+    return out
+
+
+def ring_share_fwd(q: torch.Tensor, k_blocks, v_blocks, positions, rank: int, scale: float,
+                   out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                   tile_out: torch.Tensor | None = None, tile_lse: torch.Tensor | None = None):
+    """Rank ``rank``'s share over the C ring steps, back to back on the current stream.
+
+    Step i attends the K/V block of owner (rank - i) mod C ("On Context Parallelism",
+    Peer-to-peer / Forward): ``k_blocks[o]``, ``v_blocks[o]`` and ``positions[o]`` are owner
+    o's shard and its global positions; ``positions[rank]`` are also the query positions.
+    Step 0 writes the accumulator directly; each later step writes a tile and folds it in
+    with ``lse_merge``.  Returns (out, lse).
+    """
+    C = len(k_blocks)
+    B, s, Hq, D = q.shape
+    if out is None:
+        out = torch.empty((B, s, Hq, D), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, s), dtype=torch.float32, device=q.device)
+    if C > 1:
+        if tile_out is None:
+            tile_out = torch.empty_like(out)
+        if tile_lse is None:
+            tile_lse = torch.empty_like(lse)
+    for step in range(C):
+        owner = (rank - step) % C
+        if step == 0:
+            block_fwd(q, k_blocks[owner], v_blocks[owner], positions[rank], positions[owner], scale, out, lse)
+        else:
+            block_fwd(q, k_blocks[owner], v_blocks[owner], positions[rank], positions[owner], scale,
+                      tile_out, tile_lse)
+            lse_merge(out, lse, tile_out, tile_lse)
+    return out, lse

@@ -1,0 +1,188 @@
+// C ABI of libcpattn.so: argument validation on the host, then one or more kernel launches
+// on the caller's stream.  Nothing here allocates, frees or synchronises.  A call that fails
+// validation returns before touching the GPU.  See include/cpattn.h for the contract of
+// each entry point.
+#include "cpattn.h"
+#include "cpattn_internal.h"
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#define CPATTN_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+cpattn_status_t fail(cpattn_status_t s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+cpattn_status_t ok() {
+    g_last_error[0] = '\0';
+    return CPATTN_OK;
+}
+
+cpattn_status_t from_hip(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(CPATTN_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+constexpr int64_t kMaxGrid = 2147483647;  // grid.x limit
+
+}  // namespace
+
+CPATTN_API const char* cpattn_status_string(cpattn_status_t s) {
+    switch (s) {
+        case CPATTN_OK: return "CPATTN_OK";
+        case CPATTN_ERR_INVALID_ARG: return "CPATTN_ERR_INVALID_ARG";
+        case CPATTN_ERR_SHAPE: return "CPATTN_ERR_SHAPE";
+        case CPATTN_ERR_UNSUPPORTED: return "CPATTN_ERR_UNSUPPORTED";
+        case CPATTN_ERR_HIP: return "CPATTN_ERR_HIP";
+    }
+    return "CPATTN_ERR_UNKNOWN";
+}
+
+CPATTN_API const char* cpattn_last_error(void) { return g_last_error; }
+
+CPATTN_API int32_t cpattn_abi_version(void) { return 1; }
+
+CPATTN_API cpattn_status_t cpattn_zigzag_index(int64_t seq_len, int32_t cp_size, int32_t rank,
+                                               int64_t* positions, void* stream) {
+    if (seq_len <= 0) return fail(CPATTN_ERR_INVALID_ARG, "zigzag_index: seq_len must be > 0");
+    if (cp_size <= 0) return fail(CPATTN_ERR_INVALID_ARG, "zigzag_index: cp_size must be > 0");
+    if (rank < 0 || rank >= cp_size)
+        return fail(CPATTN_ERR_INVALID_ARG, "zigzag_index: rank %d outside [0, %d)", rank, cp_size);
+    if (!positions) return fail(CPATTN_ERR_INVALID_ARG, "zigzag_index: positions is NULL");
+    if (seq_len % (2 * (int64_t)cp_size) != 0)
+        return fail(CPATTN_ERR_SHAPE, "zigzag_index: seq_len %lld not divisible by 2*cp_size = %lld",
+                    (long long)seq_len, 2LL * cp_size);
+    const int64_t t = seq_len / (2 * (int64_t)cp_size);
+    return from_hip(cpattn::launch_zigzag_index(t, rank, 2 * (int64_t)cp_size - 1 - rank, positions,
+                                                (hipStream_t)stream),
+                    "zigzag_index");
+}
+
+CPATTN_API cpattn_status_t cpattn_block_fwd(const void* q, const void* k, const void* v,
+                                            cpattn_dtype_t dtype, int32_t batch, int64_t seq_q,
+                                            int64_t seq_kv, int32_t heads_q, int32_t heads_kv,
+                                            int32_t head_dim, const int64_t* q_positions,
+                                            const int64_t* kv_positions, float scale, float* out,
+                                            float* lse, void* stream) {
+    if (dtype != CPATTN_F32 && dtype != CPATTN_BF16)
+        return fail(CPATTN_ERR_INVALID_ARG, "block_fwd: unknown dtype %d", (int)dtype);
+    if (batch <= 0 || heads_q <= 0 || heads_kv <= 0)
+        return fail(CPATTN_ERR_INVALID_ARG, "block_fwd: batch and head counts must be > 0");
+    if (seq_q < 0 || seq_kv < 0)
+        return fail(CPATTN_ERR_INVALID_ARG, "block_fwd: sequence lengths must be >= 0");
+    if (!(scale > 0.f) || !isfinite(scale))
+        return fail(CPATTN_ERR_INVALID_ARG, "block_fwd: scale must be finite and > 0");
+    if (heads_q % heads_kv != 0)
+        return fail(CPATTN_ERR_SHAPE, "block_fwd: heads_q %d not a multiple of heads_kv %d", heads_q,
+                    heads_kv);
+    if (head_dim != 64 && head_dim != 128)
+        return fail(CPATTN_ERR_UNSUPPORTED, "block_fwd: head_dim %d (supported: 64, 128)", head_dim);
+    if (dtype == CPATTN_BF16 && head_dim != 128)
+        return fail(CPATTN_ERR_UNSUPPORTED, "block_fwd: bf16 path supports head_dim 128 only");
+    if (seq_q == 0) return ok();
+    if (!q || !q_positions || !out || !lse)
+        return fail(CPATTN_ERR_INVALID_ARG, "block_fwd: q, q_positions, out and lse must be non-NULL");
+    if (seq_kv > 0 && (!k || !v || !kv_positions))
+        return fail(CPATTN_ERR_INVALID_ARG, "block_fwd: k, v and kv_positions must be non-NULL");
+    if (dtype == CPATTN_BF16 &&
+        (!aligned16(q) || (seq_kv > 0 && (!aligned16(k) || !aligned16(v))) || !aligned16(out)))
+        return fail(CPATTN_ERR_UNSUPPORTED, "block_fwd: bf16 path needs 16-byte aligned q, k, v, out");
+    if (dtype == CPATTN_F32 && ((seq_q + 63) / 64 > kMaxGrid || heads_q > 65535 || batch > 65535))
+        return fail(CPATTN_ERR_UNSUPPORTED, "block_fwd: launch grid too large");
+    if (dtype == CPATTN_BF16 && (seq_q + 31) / 32 * (int64_t)batch * heads_kv > kMaxGrid)
+        return fail(CPATTN_ERR_UNSUPPORTED, "block_fwd: launch grid too large");
+    cpattn::BlockFwdArgs a{q,     k,      v,       q_positions, kv_positions, out,      lse,
+                           batch, seq_q, seq_kv, heads_q,     heads_kv,     head_dim, scale};
+    if (seq_kv == 0) {
+        // no keys at all: every row is empty (out = 0, lse = -inf)
+        return from_hip(cpattn::launch_block_fwd_empty(a, (hipStream_t)stream), "block_fwd");
+    }
+    const hipError_t e = (dtype == CPATTN_BF16) ? cpattn::launch_block_fwd_bf16(a, (hipStream_t)stream)
+                                                : cpattn::launch_block_fwd_f32(a, (hipStream_t)stream);
+    return from_hip(e, "block_fwd");
+}
+
+CPATTN_API cpattn_status_t cpattn_lse_merge(float* out, float* lse, const float* out_tile,
+                                            const float* lse_tile, int32_t batch, int64_t seq,
+                                            int32_t heads, int32_t head_dim, void* stream) {
+    if (batch <= 0 || heads <= 0 || head_dim <= 0)
+        return fail(CPATTN_ERR_INVALID_ARG, "lse_merge: batch, heads and head_dim must be > 0");
+    if (seq < 0) return fail(CPATTN_ERR_INVALID_ARG, "lse_merge: seq must be >= 0");
+    if (head_dim % 4 != 0) return fail(CPATTN_ERR_SHAPE, "lse_merge: head_dim %d not a multiple of 4", head_dim);
+    if (head_dim > 4096) return fail(CPATTN_ERR_UNSUPPORTED, "lse_merge: head_dim %d above 4096", head_dim);
+    if (seq == 0) return ok();
+    if (!out || !lse || !out_tile || !lse_tile)
+        return fail(CPATTN_ERR_INVALID_ARG, "lse_merge: NULL pointer");
+    if (!aligned16(out) || !aligned16(out_tile))
+        return fail(CPATTN_ERR_UNSUPPORTED, "lse_merge: out and out_tile must be 16-byte aligned");
+    if (out == out_tile || lse == lse_tile)
+        return fail(CPATTN_ERR_INVALID_ARG, "lse_merge: the tile must not alias the accumulator");
+    if (((int64_t)batch * seq * heads + 63) / 64 > kMaxGrid)
+        return fail(CPATTN_ERR_UNSUPPORTED, "lse_merge: launch grid too large");
+    return from_hip(cpattn::launch_lse_merge(out, lse, out_tile, lse_tile, batch, seq, heads, head_dim,
+                                             (hipStream_t)stream),
+                    "lse_merge");
+}
+
+CPATTN_API cpattn_status_t cpattn_reorder_gathered(const void* in, void* out, int32_t batch,
+                                                   int64_t seq_len, int64_t row_bytes,
+                                                   int32_t cp_size, cpattn_reorder_dir_t dir,
+                                                   void* stream) {
+    if (batch <= 0 || seq_len <= 0 || row_bytes <= 0 || cp_size <= 0)
+        return fail(CPATTN_ERR_INVALID_ARG, "reorder_gathered: sizes must be > 0");
+    if (dir != CPATTN_RANK_TO_SEQ && dir != CPATTN_SEQ_TO_RANK)
+        return fail(CPATTN_ERR_INVALID_ARG, "reorder_gathered: unknown direction %d", (int)dir);
+    if (!in || !out) return fail(CPATTN_ERR_INVALID_ARG, "reorder_gathered: NULL pointer");
+    if (in == out) return fail(CPATTN_ERR_INVALID_ARG, "reorder_gathered: in and out must differ");
+    if (seq_len % (2 * (int64_t)cp_size) != 0)
+        return fail(CPATTN_ERR_SHAPE, "reorder_gathered: seq_len %lld not divisible by 2*cp_size = %lld",
+                    (long long)seq_len, 2LL * cp_size);
+    if (2LL * cp_size > 65535 || batch > 65535)
+        return fail(CPATTN_ERR_UNSUPPORTED, "reorder_gathered: cp_size or batch too large");
+    const int64_t chunk_bytes = seq_len / (2 * (int64_t)cp_size) * row_bytes;
+    if (chunk_bytes / 1024 + 1 > kMaxGrid)
+        return fail(CPATTN_ERR_UNSUPPORTED, "reorder_gathered: chunk too large");
+    return from_hip(cpattn::launch_reorder_gathered(in, out, batch, seq_len, row_bytes, cp_size, (int32_t)dir,
+                                                    (hipStream_t)stream),
+                    "reorder_gathered");
+}
+
+CPATTN_API cpattn_status_t cpattn_ulysses_permute(const void* in, void* out, int32_t elem_bytes,
+                                                  int32_t batch, int64_t seq_len, int32_t heads,
+                                                  int32_t head_dim, int32_t cp_size, int32_t group,
+                                                  cpattn_permute_dir_t dir, void* stream) {
+    if (elem_bytes <= 0 || batch <= 0 || seq_len <= 0 || heads <= 0 || head_dim <= 0 || cp_size <= 0)
+        return fail(CPATTN_ERR_INVALID_ARG, "ulysses_permute: sizes must be > 0");
+    if (dir != CPATTN_SEQ_TO_HEADS && dir != CPATTN_HEADS_TO_SEQ)
+        return fail(CPATTN_ERR_INVALID_ARG, "ulysses_permute: unknown direction %d", (int)dir);
+    if (group < 0 || group >= cp_size)
+        return fail(CPATTN_ERR_INVALID_ARG, "ulysses_permute: group %d outside [0, %d)", group, cp_size);
+    if (!in || !out) return fail(CPATTN_ERR_INVALID_ARG, "ulysses_permute: NULL pointer");
+    if (in == out) return fail(CPATTN_ERR_INVALID_ARG, "ulysses_permute: in and out must differ");
+    if (seq_len % cp_size != 0)
+        return fail(CPATTN_ERR_SHAPE, "ulysses_permute: seq_len %lld not divisible by cp_size %d",
+                    (long long)seq_len, cp_size);
+    if (heads % cp_size != 0)
+        return fail(CPATTN_ERR_SHAPE, "ulysses_permute: heads %d not divisible by cp_size %d", heads,
+                    cp_size);
+    const int64_t seg_bytes = (int64_t)(heads / cp_size) * head_dim * elem_bytes;
+    const int64_t span_bytes = seq_len / cp_size * seg_bytes;
+    if (span_bytes >= (1LL << 31) || (int64_t)cp_size * batch > 65535)
+        return fail(CPATTN_ERR_UNSUPPORTED, "ulysses_permute: one shard's head group exceeds 2 GiB or "
+                                            "cp_size*batch exceeds 65535");
+    return from_hip(cpattn::launch_ulysses_permute(in, out, elem_bytes, batch, seq_len, heads, head_dim,
+                                                   cp_size, group, (int32_t)dir, (hipStream_t)stream),
+                    "ulysses_permute");
+}

@@ -1,0 +1,419 @@
+// bf16 block attention on the gfx950 matrix cores.
+//
+// What it computes ("On Context Parallelism", section Peer-to-peer / Forward: the attention
+// call of one ring step on global positions, returning the normalised block output and its
+// log-sum-exp; "Context Parallelism & Ring Attention", section Softmax is decomposable:
+// the running max / sum / output recurrence over key blocks):
+//   for each (b, query head h, local row i), over keys j of this block with
+//   kv_pos[j] <= q_pos[i]:  out_i = softmax_j(scale <q_i, k_j>) v_j,  lse_i = ln sum_j e^(s_ij).
+//
+// Work decomposition.  A block (256 threads = 4 waves) owns G query heads that share one
+// K/V head (G = 4, 2 or 1, whichever divides heads_q/heads_kv) times PQ = 128*NB/G query
+// positions.  Each wave owns NB "column blocks" of 32 query rows; every lane holds one
+// query row of each column block.
+//
+// Per K/V tile of 64 keys:
+//   S^T = K Q^T    with v_mfma_f32_32x32x16_bf16: A = 32 keys x 16 dims of K (LDS),
+//                  B = 16 dims x 32 queries of Q (registers, loaded once).
+//                  The accumulator gives each lane 16 keys of ONE query, so the row max and
+//                  row sum are lane-local plus one exchange with the other half-wave.
+//   online softmax in the log2 domain (scores pre-multiplied by scale*log2(e), exp2),
+//   P rounded to bf16 (RNE) straight from the accumulator registers,
+//   O^T += V^T P^T with A = 32 dims x 16 keys of V read transposed from the row-major LDS
+//                  tile by ds_read_b64_tr_b16, B = P^T (registers).  The key order inside a
+//                  16-key step is the accumulator's own order, applied to V's addresses.
+// K and V tiles are double-buffered in LDS (XOR-swizzled 16-byte chunks, conflict-free
+// for both the row reads of K and the transposed reads of V); the next tile's global loads
+// are in flight while the current tile is computed.
+//
+// Causal skip ("Context parallelism: Ring Attention and Ulysses", Ring Attention: blocks
+// later than the query are skipped whole): with strictly increasing positions the visible
+// tiles of a block are a prefix, and the tiles entirely visible to every query of the block
+// are a shorter prefix; only the tiles in between are masked element by element.
+// Rows with no visible key end with out = 0 and lse = -inf.
+#include "cpattn_internal.h"
+
+#include <math.h>
+
+namespace cpattn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr int kD = 128;             // head dim
+constexpr int kBN = 64;             // keys per tile
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRowBytes = kD * 2;   // one K/V row in LDS
+constexpr int kTileBytes = kBN * kRowBytes;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+struct Params {
+    const __bf16* q;
+    const __bf16* k;
+    const __bf16* v;
+    const int64_t* qpos;
+    const int64_t* kvpos;
+    float* out;
+    float* lse;
+    int64_t seq_q;
+    int64_t seq_kv;
+    int64_t n_qt;      // query tiles of PQ positions
+    int32_t heads_q;
+    int32_t heads_kv;
+    int32_t ratio;     // heads_q / heads_kv
+    int32_t G;         // query heads per block
+    int32_t pq;        // query positions per block
+    int32_t n_hg;      // ratio / G head groups per kv head
+    int32_t n_cols;    // batch * heads_kv * n_hg
+    int32_t xcd_cols;  // n_cols / 8 when n_cols % 8 == 0, else 0
+    float c;           // scale * log2(e)
+};
+
+__device__ inline int wave_sum(int x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+
+// Value of the other half-wave (lane ^ 32) combined with our own: both outputs of the
+// half-swap hold {ours, theirs}.
+__device__ inline float half_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float half_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ inline bf16x8 lds_b128(const LDS_AS char* p) { return *(const LDS_AS bf16x8*)p; }
+
+__device__ inline bf16x8 lds_tr_pair(const LDS_AS char* p0, const LDS_AS char* p1) {
+    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)p0);
+    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)p1);
+    const s16x8 c = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return __builtin_bit_cast(bf16x8, c);
+}
+
+__device__ inline bf16x8 pack_bf16(const f32x16& s, int base) {
+    bf16x8 r;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r[j] = (__bf16)s[base + j];
+    return r;
+}
+
+template <int NB>
+__global__ void __launch_bounds__(kThreads, 1) block_fwd_bf16_kernel(const Params p) {
+    __shared__ __attribute__((aligned(16))) char lds_raw[4 * kTileBytes];  // [buf][K|V][tile]
+    __shared__ int red[2 * kWaves];
+    LDS_AS char* lds = (LDS_AS char*)lds_raw;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const int half = lane >> 5;
+    const int l32 = lane & 31;
+
+    // ---- which (b, kv head, head group, query tile) this block owns; heavy tiles first
+    int col;
+    int64_t qt_rank;
+    if (p.xcd_cols > 0) {
+        // consecutive blocks are dealt round-robin to the 8 XCDs: keep one XCD on the same
+        // columns (same K/V head) so its L2 serves all of them
+        const int x = blockIdx.x & 7;
+        const int64_t kk = blockIdx.x >> 3;
+        qt_rank = kk / p.xcd_cols;
+        col = x + 8 * (int)(kk % p.xcd_cols);
+    } else {
+        col = (int)(blockIdx.x % p.n_cols);
+        qt_rank = blockIdx.x / p.n_cols;
+    }
+    const int64_t qt = p.n_qt - 1 - qt_rank;
+    const int hg = col % p.n_hg;
+    const int kvh = (col / p.n_hg) % p.heads_kv;
+    const int64_t b = col / (p.n_hg * p.heads_kv);
+
+    const int64_t q0 = qt * p.pq;
+    const int64_t q_last = (q0 + p.pq < p.seq_q ? q0 + p.pq : p.seq_q) - 1;
+    const int64_t pmin = p.qpos[q0];
+    const int64_t pmax = p.qpos[q_last];
+
+    // ---- visible tiles (a prefix) and tiles visible to every query of the block
+    const int64_t n_tiles = (p.seq_kv + kBN - 1) / kBN;
+    int c_ne = 0, c_full = 0;
+    for (int64_t t = tid; t < n_tiles; t += kThreads) {
+        c_ne += (p.kvpos[t * kBN] <= pmax) ? 1 : 0;
+        const int64_t lk = t * kBN + kBN - 1;
+        c_full += (lk < p.seq_kv && p.kvpos[lk] <= pmin) ? 1 : 0;
+    }
+    c_ne = wave_sum(c_ne);
+    c_full = wave_sum(c_full);
+    if (lane == 0) {
+        red[w] = c_ne;
+        red[kWaves + w] = c_full;
+    }
+    __syncthreads();
+    int n_ne = 0, n_full = 0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+        n_ne += red[i];
+        n_full += red[kWaves + i];
+    }
+
+    // ---- this lane's query rows; Q as MFMA B operands (16 dims x 32 queries per step)
+    bf16x8 qreg[NB][kD / 16];
+    int64_t myq[NB];
+    int64_t myh[NB];
+    int64_t mypos[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int row0 = (w * NB + nb) * 32;
+        const int hs = row0 / p.pq;
+        const int64_t i = q0 + (row0 % p.pq) + l32;
+        const int64_t head = (int64_t)kvh * p.ratio + (int64_t)hg * p.G + hs;
+        myq[nb] = i;
+        myh[nb] = head;
+        const bool valid = i < p.seq_q;
+        mypos[nb] = valid ? p.qpos[i] : INT64_MIN;
+        const __bf16* qrow = p.q + ((b * p.seq_q + (valid ? i : 0)) * p.heads_q + head) * kD + 8 * half;
+#pragma unroll
+        for (int ks = 0; ks < kD / 16; ++ks) {
+            u32x4 raw = valid ? *(const u32x4*)(qrow + 16 * ks) : u32x4{0, 0, 0, 0};
+            qreg[nb][ks] = __builtin_bit_cast(bf16x8, raw);
+        }
+    }
+
+    f32x16 acc_o[NB][kD / 32];
+    float m_run[NB], l_run[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        m_run[nb] = -INFINITY;
+        l_run[nb] = 0.f;
+#pragma unroll
+        for (int db = 0; db < kD / 32; ++db) acc_o[nb][db] = f32x16{};
+    }
+
+    // ---- per-lane LDS offsets
+    // K (row reads): key = 32*kb + l32, 16-byte chunk (2*ks + half) XOR (key & 15)
+    uint32_t off_k[kD / 16];
+#pragma unroll
+    for (int ks = 0; ks < kD / 16; ++ks)
+        off_k[ks] = l32 * kRowBytes + (((2 * ks + half) ^ (lane & 15)) << 4);
+    // V (transposed reads): in each 16-lane group, lane s reads 4 dims starting at
+    // 16*(group&1) + 4*(s&3) of key (s>>2) + 4*half (+8 for the second read);
+    // chunk XOR ((key & 7) << 1)
+    const int grp = lane >> 4, s16 = lane & 15;
+    const int vkey = 4 * half + (s16 >> 2);
+    const int vsw = (vkey & 7) << 1;
+    uint32_t off_v[kD / 32];
+#pragma unroll
+    for (int db = 0; db < kD / 32; ++db) {
+        const int chunk = 4 * db + 2 * (grp & 1) + ((s16 & 3) >> 1);
+        off_v[db] = vkey * kRowBytes + ((chunk ^ vsw) << 4) + ((s16 & 1) << 3);
+    }
+
+    // ---- global -> register staging of one K/V tile: thread owns 16-byte chunk (tid & 15)
+    // of keys 16*i + (tid >> 4), i = 0..3, for K and V
+    const __bf16* kbase = p.k + (b * p.seq_kv * p.heads_kv + kvh) * (int64_t)kD;
+    const __bf16* vbase = p.v + (b * p.seq_kv * p.heads_kv + kvh) * (int64_t)kD;
+    const int64_t kstride = (int64_t)p.heads_kv * kD;
+    const int st_chunk = tid & 15;
+    const int st_key = tid >> 4;
+    u32x4 stage_k[4], stage_v[4];
+
+    auto load_tile = [&](int jt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t j = (int64_t)jt * kBN + 16 * i + st_key;
+            if (j < p.seq_kv) {
+                stage_k[i] = *(const u32x4*)(kbase + j * kstride + st_chunk * 8);
+                stage_v[i] = *(const u32x4*)(vbase + j * kstride + st_chunk * 8);
+            } else {
+                stage_k[i] = u32x4{0, 0, 0, 0};
+                stage_v[i] = u32x4{0, 0, 0, 0};
+            }
+        }
+    };
+    auto store_tile = [&](int buf) {
+        LDS_AS char* kt = lds + buf * 2 * kTileBytes;
+        LDS_AS char* vt = kt + kTileBytes;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int key = 16 * i + st_key;
+            *(LDS_AS u32x4*)(kt + key * kRowBytes + ((st_chunk ^ (key & 15)) << 4)) = stage_k[i];
+            *(LDS_AS u32x4*)(vt + key * kRowBytes + ((st_chunk ^ ((key & 7) << 1)) << 4)) = stage_v[i];
+        }
+    };
+
+    if (n_ne > 0) {
+        load_tile(0);
+        store_tile(0);
+    }
+    __syncthreads();
+
+    for (int jt = 0; jt < n_ne; ++jt) {
+        const int buf = jt & 1;
+        const bool more = jt + 1 < n_ne;
+        if (more) load_tile(jt + 1);
+        const LDS_AS char* kt = lds + buf * 2 * kTileBytes;
+        const LDS_AS char* vt = kt + kTileBytes;
+
+        // S^T = K Q^T
+        f32x16 s[NB][2];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            s[nb][0] = f32x16{};
+            s[nb][1] = f32x16{};
+        }
+#pragma unroll
+        for (int ks = 0; ks < kD / 16; ++ks) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const bf16x8 a = lds_b128(kt + kb * 32 * kRowBytes + off_k[ks]);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    s[nb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[nb][ks], s[nb][kb], 0, 0, 0);
+            }
+        }
+
+        // element mask on tiles not entirely visible: key index of accumulator entry v is
+        // 32*kb + 8*(v/4) + 4*half + v%4
+        if (jt >= n_full) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                for (int vv = 0; vv < 16; ++vv) {
+                    const int64_t j = (int64_t)jt * kBN + 32 * kb + 8 * (vv >> 2) + 4 * half + (vv & 3);
+                    const int64_t kp = (j < p.seq_kv) ? p.kvpos[j] : INT64_MAX;
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+                        if (kp > mypos[nb]) s[nb][kb][vv] = -INFINITY;
+                }
+            }
+        }
+
+        // online softmax, log2 domain; P^T as MFMA B operands straight from registers
+        bf16x8 pb[NB][2][2];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int vv = 0; vv < 16; ++vv) mx = fmaxf(mx, s[nb][kb][vv]);
+            mx = half_max(mx);
+            const float m_new = fmaxf(m_run[nb], mx * p.c);
+            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+            const float alpha = __builtin_amdgcn_exp2f(m_run[nb] - m_use);
+            float rs = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int vv = 0; vv < 16; ++vv) {
+                    const float e = __builtin_amdgcn_exp2f(fmaf(s[nb][kb][vv], p.c, -m_use));
+                    s[nb][kb][vv] = e;
+                    rs += e;
+                }
+            l_run[nb] = l_run[nb] * alpha + rs;
+            m_run[nb] = m_new;
+#pragma unroll
+            for (int db = 0; db < kD / 32; ++db) acc_o[nb][db] *= alpha;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                pb[nb][kb][0] = pack_bf16(s[nb][kb], 0);
+                pb[nb][kb][1] = pack_bf16(s[nb][kb], 8);
+            }
+        }
+
+        // O^T += V^T P^T
+#pragma unroll
+        for (int db = 0; db < kD / 32; ++db) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                for (int ks2 = 0; ks2 < 2; ++ks2) {
+                    const LDS_AS char* base = vt + (32 * kb + 16 * ks2) * kRowBytes + off_v[db];
+                    const bf16x8 a = lds_tr_pair(base, base + 8 * kRowBytes);
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+                        acc_o[nb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[nb][kb][ks2], acc_o[nb][db], 0, 0, 0);
+                }
+            }
+        }
+
+        if (more) store_tile(buf ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue: combine the half-wave row sums, normalise, store
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const float l_tot = half_sum(l_run[nb]);
+        const bool any = l_tot > 0.f;
+        const float inv = any ? 1.f / l_tot : 0.f;
+        if (myq[nb] >= p.seq_q) continue;
+        float* orow = p.out + ((b * p.seq_q + myq[nb]) * p.heads_q + myh[nb]) * kD;
+#pragma unroll
+        for (int db = 0; db < kD / 32; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                float4 o4;
+                o4.x = acc_o[nb][db][4 * g + 0] * inv;
+                o4.y = acc_o[nb][db][4 * g + 1] * inv;
+                o4.z = acc_o[nb][db][4 * g + 2] * inv;
+                o4.w = acc_o[nb][db][4 * g + 3] * inv;
+                *(float4*)(orow + 32 * db + 8 * g + 4 * half) = o4;
+            }
+        if (half == 0)
+            p.lse[(b * p.heads_q + myh[nb]) * p.seq_q + myq[nb]] =
+                any ? (m_run[nb] + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_block_fwd_bf16(const BlockFwdArgs& a, hipStream_t stream) {
+    Params p;
+    p.q = (const __bf16*)a.q;
+    p.k = (const __bf16*)a.k;
+    p.v = (const __bf16*)a.v;
+    p.qpos = a.q_pos;
+    p.kvpos = a.kv_pos;
+    p.out = a.out;
+    p.lse = a.lse;
+    p.seq_q = a.seq_q;
+    p.seq_kv = a.seq_kv;
+    p.heads_q = a.heads_q;
+    p.heads_kv = a.heads_kv;
+    p.ratio = a.heads_q / a.heads_kv;
+    p.G = (p.ratio % 4 == 0) ? 4 : (p.ratio % 2 == 0) ? 2 : 1;
+    p.n_hg = p.ratio / p.G;
+    p.n_cols = a.batch * a.heads_kv * p.n_hg;
+    p.xcd_cols = (p.n_cols % 8 == 0) ? p.n_cols / 8 : 0;
+    p.c = a.scale * kLog2e;
+    // two column blocks per wave unless that leaves the chip less than half full
+    int nb = 2;
+    {
+        const int64_t pq2 = 128 * 2 / p.G;
+        const int64_t blocks2 = ((a.seq_q + pq2 - 1) / pq2) * p.n_cols;
+        if (blocks2 < 512) nb = 1;
+    }
+    p.pq = 128 * nb / p.G;
+    p.n_qt = (a.seq_q + p.pq - 1) / p.pq;
+    const int64_t blocks = p.n_qt * p.n_cols;
+    if (nb == 2)
+        hipLaunchKernelGGL(block_fwd_bf16_kernel<2>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL(block_fwd_bf16_kernel<1>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace cpattn

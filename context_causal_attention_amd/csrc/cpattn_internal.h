@@ -1,0 +1,50 @@
+// Internal launch interface between the C ABI layer (api.hip) and the kernels.
+// Every launcher assumes its arguments were validated by the ABI layer and only enqueues
+// work on `stream`; it returns the launch status from hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cpattn {
+
+hipError_t launch_zigzag_index(int64_t chunk_len, int64_t early_chunk, int64_t late_chunk,
+                               int64_t* positions, hipStream_t stream);
+
+hipError_t launch_lse_merge(float* out, float* lse, const float* out_tile, const float* lse_tile,
+                            int32_t batch, int64_t seq, int32_t heads, int32_t head_dim,
+                            hipStream_t stream);
+
+hipError_t launch_reorder_gathered(const void* in, void* out, int32_t batch, int64_t seq_len,
+                                   int64_t row_bytes, int32_t cp_size, int32_t dir,
+                                   hipStream_t stream);
+
+hipError_t launch_ulysses_permute(const void* in, void* out, int32_t elem_bytes, int32_t batch,
+                                  int64_t seq_len, int32_t heads, int32_t head_dim,
+                                  int32_t cp_size, int32_t group, int32_t dir, hipStream_t stream);
+
+struct BlockFwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const int64_t* q_pos;
+    const int64_t* kv_pos;
+    float* out;
+    float* lse;
+    int32_t batch;
+    int64_t seq_q;
+    int64_t seq_kv;
+    int32_t heads_q;
+    int32_t heads_kv;
+    int32_t head_dim;
+    float scale;
+};
+
+// No keys: writes out = 0 and lse = -inf for every row.
+hipError_t launch_block_fwd_empty(const BlockFwdArgs& a, hipStream_t stream);
+// fp32 inputs, fp32 arithmetic on the vector ALUs.
+hipError_t launch_block_fwd_f32(const BlockFwdArgs& a, hipStream_t stream);
+// bf16 inputs, bf16 matrix-core products with fp32 accumulation.
+hipError_t launch_block_fwd_bf16(const BlockFwdArgs& a, hipStream_t stream);
+
+}  // namespace cpattn

@@ -1,0 +1,81 @@
+// In-place merge of a completed partial attention result into an accumulator.
+// "On Context Parallelism", section Peer-to-peer (merging attention tiles): the merged
+// log-sum-exp is ln(e^lse + e^lse_tile) and each side's output is weighted by
+// e^(its lse - merged).  An empty side (lse = -inf) weighs 0; two empty sides give (0, -inf).
+//
+// Bandwidth-bound: per row of head_dim floats it reads out and out_tile and writes out.
+// A block owns ROWS consecutive (b, i, h) rows: it first turns their lse pairs into the two
+// weights (in LDS), then streams the rows with 16-byte accesses.
+#include "cpattn_internal.h"
+
+#include <math.h>
+
+namespace cpattn {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRows = 64;
+
+// ln(e^a + e^b), symmetric in a and b; -inf when both are -inf.
+__device__ inline float log_add_exp(float a, float b) {
+    const float hi = fmaxf(a, b), lo = fminf(a, b);
+    if (hi == -INFINITY) return -INFINITY;
+    return hi + log1pf(expf(lo - hi));
+}
+
+__global__ void __launch_bounds__(kThreads) lse_merge_kernel(
+    float* __restrict__ out, float* __restrict__ lse, const float* __restrict__ out_t,
+    const float* __restrict__ lse_t, int64_t seq, int32_t heads, int32_t head_dim, int64_t n_rows) {
+    __shared__ float w_old[kRows];
+    __shared__ float w_new[kRows];
+    const int64_t row0 = (int64_t)blockIdx.x * kRows;
+    const int tid = threadIdx.x;
+    if (tid < kRows && row0 + tid < n_rows) {
+        // row = (b*seq + i)*heads + h  <->  lse index (b*heads + h)*seq + i
+        const int64_t row = row0 + tid;
+        const int64_t h = row % heads;
+        const int64_t bi = row / heads;
+        const int64_t i = bi % seq, b = bi / seq;
+        const int64_t li = (b * heads + h) * seq + i;
+        const float a = lse[li], c = lse_t[li];
+        const float m = log_add_exp(a, c);
+        const bool empty = (m == -INFINITY);
+        w_old[tid] = empty ? 0.f : expf(a - m);
+        w_new[tid] = empty ? 0.f : expf(c - m);
+        lse[li] = m;
+    }
+    __syncthreads();
+    const int vec_per_row = head_dim / 4;
+    const int rows_here = (int)((n_rows - row0) < kRows ? (n_rows - row0) : kRows);
+    const int n_vec = rows_here * vec_per_row;
+    float4* o4 = reinterpret_cast<float4*>(out + row0 * head_dim);
+    const float4* t4 = reinterpret_cast<const float4*>(out_t + row0 * head_dim);
+    for (int e = tid; e < n_vec; e += kThreads) {
+        // two rounded products and a rounded sum (contraction into a fused multiply-add is
+        // off), so the result does not depend on which operand is the accumulator
+#pragma clang fp contract(off)
+        const int r = e / vec_per_row;
+        const float a = w_old[r], c = w_new[r];
+        const float4 x = o4[e], y = t4[e];
+        float4 z;
+        z.x = a * x.x + c * y.x;
+        z.y = a * x.y + c * y.y;
+        z.z = a * x.z + c * y.z;
+        z.w = a * x.w + c * y.w;
+        o4[e] = z;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_lse_merge(float* out, float* lse, const float* out_tile, const float* lse_tile,
+                            int32_t batch, int64_t seq, int32_t heads, int32_t head_dim,
+                            hipStream_t stream) {
+    const int64_t n_rows = (int64_t)batch * seq * heads;
+    const int64_t blocks = (n_rows + kRows - 1) / kRows;
+    hipLaunchKernelGGL(lse_merge_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, out, lse,
+                       out_tile, lse_tile, seq, heads, head_dim, n_rows);
+    return hipGetLastError();
+}
+
+}  // namespace cpattn

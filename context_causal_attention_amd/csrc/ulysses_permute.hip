@@ -1,0 +1,91 @@
+// Local layout change of Ulysses context parallelism for one head group.
+// "Appendix F: Context Parallelism and MoE Parallel Folding", Eq. (96): [B, S/C, H, d] per
+// rank becomes [B, S, H/C, d]; "On Context Parallelism", section All-to-all; "Context
+// parallelism: Ring Attention and Ulysses", section Ulysses: group g = heads
+// [g*H/C, (g+1)*H/C), and sequence shard src supplies rows [src*S/C, (src+1)*S/C).
+//
+// For one (src, b) pair the move is a 2-D copy of s = S/C rows of one head-group segment
+// (H/C * D * elem bytes): in the stacked shards [C][B][S/C][H][D] the rows are H*D*elem
+// apart, in the grouped tensor [B][S][H/C][D] they are packed.  grid.y enumerates (src, b),
+// grid.x spans the s*seg elements of that copy.  Bandwidth-bound: 16-byte accesses when
+// sizes and pointers allow (byte accesses otherwise); the row/offset split uses a 32-bit
+// division by an invariant divisor (multiply-high with a precomputed magic number).
+#include "cpattn_internal.h"
+
+namespace cpattn {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kVecPerThread = 4;
+
+// Exact n / d for 0 <= n < 2^31 and 1 <= d < 2^31 (Granlund & Montgomery, "Division by
+// invariant integers using multiplication", 1994): l = ceil(log2 d),
+// m = floor(2^32 (2^l - d) / d) + 1, q = (mulhi(n, m) + n) >> l.
+struct FastDiv {
+    uint32_t m, l, d;
+};
+
+FastDiv make_fastdiv(uint32_t d) {
+    uint32_t l = 0;
+    while ((1ull << l) < d) ++l;
+    const uint64_t m = ((1ull << 32) * ((1ull << l) - d)) / d + 1;
+    return FastDiv{(uint32_t)m, l, d};
+}
+
+__device__ inline uint32_t fast_div(uint32_t n, FastDiv f) {
+    return (__umulhi(n, f.m) + n) >> f.l;
+}
+
+template <typename T>
+__global__ void __launch_bounds__(kThreads) ulysses_kernel(const T* __restrict__ in, T* __restrict__ out,
+                                                           uint32_t span, FastDiv seg, int64_t row,
+                                                           int64_t head_off, int64_t S, int64_t s,
+                                                           int64_t B, int32_t dir) {
+    const int64_t sb = blockIdx.y;          // src * B + b
+    const int64_t src = sb / B, b = sb - src * B;
+    const int64_t stacked_base = sb * s * row + head_off;          // row i at + i*row
+    const int64_t grouped_base = (b * S + src * s) * (int64_t)seg.d;  // row i at + i*seg
+    const uint32_t base = blockIdx.x * (uint32_t)(kThreads * kVecPerThread) + threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < kVecPerThread; ++u) {
+        const uint32_t e = base + (uint32_t)u * kThreads;
+        if (e >= span) break;
+        const uint32_t i = fast_div(e, seg);
+        const uint32_t w = e - i * seg.d;
+        const int64_t so = stacked_base + (int64_t)i * row + w;
+        const int64_t go = grouped_base + e;
+        if (dir == 0) out[go] = in[so];
+        else out[so] = in[go];
+    }
+}
+
+}  // namespace
+
+hipError_t launch_ulysses_permute(const void* in, void* out, int32_t elem_bytes, int32_t batch,
+                                  int64_t seq_len, int32_t heads, int32_t head_dim,
+                                  int32_t cp_size, int32_t group, int32_t dir, hipStream_t stream) {
+    const int64_t hg = heads / cp_size;
+    const int64_t seg_bytes = hg * head_dim * (int64_t)elem_bytes;
+    const int64_t row_bytes = (int64_t)heads * head_dim * elem_bytes;
+    const int64_t off_bytes = (int64_t)group * seg_bytes;
+    const bool vec = (seg_bytes % 16 == 0) && (row_bytes % 16 == 0) && ((uintptr_t)in % 16 == 0) &&
+                     ((uintptr_t)out % 16 == 0);
+    const int64_t el = vec ? 16 : 1;
+    const int64_t s = seq_len / cp_size;
+    const int64_t seg = seg_bytes / el;
+    const int64_t span = s * seg;  // elements of one (src, b) copy; the ABI layer bounds it < 2^31
+    const int64_t per_block = kThreads * kVecPerThread;
+    const dim3 grid((unsigned)((span + per_block - 1) / per_block), (unsigned)(cp_size * batch));
+    const FastDiv fd = make_fastdiv((uint32_t)seg);
+    if (vec)
+        hipLaunchKernelGGL(ulysses_kernel<uint4>, grid, dim3(kThreads), 0, stream, (const uint4*)in,
+                           (uint4*)out, (uint32_t)span, fd, row_bytes / el, off_bytes / el, seq_len,
+                           s, (int64_t)batch, dir);
+    else
+        hipLaunchKernelGGL(ulysses_kernel<uint8_t>, grid, dim3(kThreads), 0, stream,
+                           (const uint8_t*)in, (uint8_t*)out, (uint32_t)span, fd, row_bytes,
+                           off_bytes, seq_len, s, (int64_t)batch, dir);
+    return hipGetLastError();
+}
+
+}  // namespace cpattn

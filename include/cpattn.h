@@ -1,0 +1,186 @@
+/*
+ * cpattn.h -- C ABI of libcpattn.so: one context-parallel rank's share of causal
+ * attention, computed blockwise on one AMD Instinct MI355X (gfx950), plus the layout
+ * companions of the all-gather and Ulysses variants.
+ *
+ * Sources (web pages; cited by title and section):
+ *   [CP]    "On Context Parallelism" (jonahsamost.bearblog.dev)
+ *   [DAY74] "Context parallelism -- splitting the sequence across GPUs" (llmdaily.org)
+ *   [RING]  "Context Parallelism & Ring Attention" (Distributed Training from First Principles)
+ *   [HB]    "Context parallelism: Ring Attention and Ulysses" (AI infra handbook)
+ *   [OLMO]  "Appendix F: Context Parallelism and MoE Parallel Folding" (olmo-core MoE report)
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - All tensor pointers are DEVICE pointers owned by the caller.  The library never
+ *   allocates, frees or synchronises; every call only enqueues kernels on `stream`
+ *   (a hipStream_t passed as void*; NULL means the null stream) and returns.
+ * - Tensors are dense, row-major, in the layouts stated per call.  Outputs must not alias
+ *   inputs, except where a call is documented as in place.
+ * - Every argument is validated on the host before anything is enqueued.  A call that
+ *   returns an error has enqueued nothing and touched no memory.  CPATTN_ERR_HIP is
+ *   returned when the HIP runtime reports an error for a launch.
+ *   cpattn_last_error() gives a human-readable reason for the last failure on the
+ *   calling thread.
+ * - Sizes are int64 and all address arithmetic is 64-bit (tensors above 2^31 elements
+ *   are supported).
+ * - The library is stateless; calls on different streams may run concurrently as long
+ *   as their buffers do not overlap.
+ */
+#ifndef CPATTN_H
+#define CPATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CPATTN_OK = 0,
+    CPATTN_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, bad enum, bad scale */
+    CPATTN_ERR_SHAPE = 2,       /* a divisibility or size relation between arguments fails */
+    CPATTN_ERR_UNSUPPORTED = 3, /* well-formed but not implemented (head_dim, dtype) */
+    CPATTN_ERR_HIP = 4          /* the HIP runtime reported an error */
+} cpattn_status_t;
+
+typedef enum { CPATTN_F32 = 0, CPATTN_BF16 = 1 } cpattn_dtype_t;
+
+typedef enum {
+    CPATTN_RANK_TO_SEQ = 0, /* all-gather (rank) order -> global sequence order */
+    CPATTN_SEQ_TO_RANK = 1  /* global sequence order -> all-gather (rank) order */
+} cpattn_reorder_dir_t;
+
+typedef enum {
+    CPATTN_SEQ_TO_HEADS = 0, /* [C][B][S/C][H][D] rank shards -> [B][S][H/C][D] of one group */
+    CPATTN_HEADS_TO_SEQ = 1  /* the inverse */
+} cpattn_permute_dir_t;
+
+/* Static string naming a status code. */
+const char* cpattn_status_string(cpattn_status_t status);
+
+/* Reason for the last failed call on this thread ("" if none).  Valid until the next
+ * call on the same thread. */
+const char* cpattn_last_error(void);
+
+/* ABI version of this header: 1. */
+int32_t cpattn_abi_version(void);
+
+/*
+ * cpattn_zigzag_index -- global positions of rank `rank`'s local tokens under zigzag
+ * sharding.  [CP] "All-gather" (and [RING] "The zigzag fix", [HB] "The zigzag
+ * partition"): the sequence is cut into 2C chunks of t = S/(2C) tokens and rank r holds
+ * chunk r followed by chunk 2C-1-r.
+ *
+ *   positions  out, int64 [seq_len / cp_size]: positions[i] = r*t + i for i < t,
+ *              (2C-1-r)*t + (i - t) otherwise.  Strictly increasing.
+ * Errors: SHAPE if seq_len % (2*cp_size) != 0; INVALID_ARG if seq_len <= 0, cp_size <= 0,
+ * rank outside [0, cp_size) or positions is NULL.
+ */
+cpattn_status_t cpattn_zigzag_index(int64_t seq_len, int32_t cp_size, int32_t rank,
+                                    int64_t* positions, void* stream);
+
+/*
+ * cpattn_block_fwd -- attention of local queries against one K/V block under a causal
+ * mask on GLOBAL positions, returning the block's normalised output and its log-sum-exp.
+ * This is the per-step attention call of the ring forward in [CP] "Peer-to-peer" /
+ * "Forward" (and the single call of [CP] "All-gather" / "Forward"):
+ *
+ *   s_ij  = scale * <q_i, k_j>            for kv_positions[j] <= q_positions[i]
+ *   lse_i = ln sum_j exp(s_ij)            (natural log; [CP] "Peer-to-peer", the lse
+ *                                          definition in the merge discussion)
+ *   out_i = sum_j exp(s_ij - lse_i) v_j
+ *
+ * A query with no visible key in this block gets out_i = 0 and lse_i = -inf, which the
+ * merge treats as "no contribution".  Grouped-query attention: query head h reads K/V
+ * head h / (heads_q / heads_kv).
+ *
+ *   q             in  [batch][seq_q][heads_q][head_dim], dtype
+ *   k, v          in  [batch][seq_kv][heads_kv][head_dim], dtype
+ *   q_positions   in  int64 [seq_q], strictly increasing (precondition, not checked;
+ *                     violating it gives unspecified values, never an out-of-bounds access)
+ *   kv_positions  in  int64 [seq_kv], strictly increasing (same)
+ *   scale         finite and > 0 (e.g. 1/sqrt(head_dim))
+ *   out           out fp32 [batch][seq_q][heads_q][head_dim]
+ *   lse           out fp32 [batch][heads_q][seq_q]
+ *
+ * dtype CPATTN_BF16: bf16 inputs, products accumulated in fp32 on the matrix cores; the
+ * softmax weights are rounded to bf16 (round to nearest even) before the second product;
+ * the row sums are kept in fp32.  dtype CPATTN_F32: fp32 throughout.
+ * head_dim must be 64 or 128.  seq_q == 0 is a no-op (pointers may be NULL); seq_kv == 0
+ * writes out = 0, lse = -inf (k, v, kv_positions may be NULL).
+ * Errors: INVALID_ARG (NULL pointer, batch/heads <= 0, seq < 0, bad scale or dtype),
+ * SHAPE (heads_q % heads_kv != 0), UNSUPPORTED (head_dim not 64/128).
+ */
+cpattn_status_t cpattn_block_fwd(const void* q, const void* k, const void* v, cpattn_dtype_t dtype,
+                                 int32_t batch, int64_t seq_q, int64_t seq_kv, int32_t heads_q,
+                                 int32_t heads_kv, int32_t head_dim, const int64_t* q_positions,
+                                 const int64_t* kv_positions, float scale, float* out, float* lse,
+                                 void* stream);
+
+/*
+ * cpattn_lse_merge -- fold one completed partial result into an accumulator, in place.
+ * [CP] "Peer-to-peer" (merging attention tiles) and [HB] "Ring Attention":
+ *
+ *   merged = ln(exp(lse) + exp(lse_tile))
+ *   out    = exp(lse - merged) * out + exp(lse_tile - merged) * out_tile
+ *   lse    = merged
+ *
+ * A side whose lse is -inf has weight 0; two empty sides give (0, -inf) and never NaN.
+ * The result is symmetric in its two operands.
+ *
+ *   out       in/out fp32 [batch][seq][heads][head_dim]
+ *   lse       in/out fp32 [batch][heads][seq]
+ *   out_tile  in     fp32 [batch][seq][heads][head_dim]
+ *   lse_tile  in     fp32 [batch][heads][seq]
+ * Errors: INVALID_ARG (NULL pointer, batch/heads/head_dim <= 0, seq < 0), SHAPE
+ * (head_dim % 4 != 0).  seq == 0 is a no-op.
+ */
+cpattn_status_t cpattn_lse_merge(float* out, float* lse, const float* out_tile,
+                                 const float* lse_tile, int32_t batch, int64_t seq,
+                                 int32_t heads, int32_t head_dim, void* stream);
+
+/*
+ * cpattn_reorder_gathered -- chunk reorder between the all-gather's rank order and the
+ * global sequence order.  [CP] "All-gather": the gather concatenates the ranks' zigzag
+ * shards in rank order (at C=4: chunks 0,7,1,6,2,5,3,4), and K/V must be put back in
+ * sequence order before attention; the backward applies the inverse permutation.
+ * Gathered slot k holds chunk k/2 (k even) or 2C-1-(k-1)/2 (k odd).
+ *
+ *   in, out    [batch][seq_len][row_bytes] (rows are opaque bytes, e.g. heads*D*2)
+ *   dir        CPATTN_RANK_TO_SEQ: out[b][chunk c] = in[b][slot of c]
+ *              CPATTN_SEQ_TO_RANK: out[b][slot k] = in[b][chunk of k]
+ * Bit-exact byte copy.  Errors: INVALID_ARG (NULL pointer, sizes <= 0, bad dir, in == out),
+ * SHAPE (seq_len % (2*cp_size) != 0).
+ */
+cpattn_status_t cpattn_reorder_gathered(const void* in, void* out, int32_t batch, int64_t seq_len,
+                                        int64_t row_bytes, int32_t cp_size,
+                                        cpattn_reorder_dir_t dir, void* stream);
+
+/*
+ * cpattn_ulysses_permute -- the local layout change around Ulysses' all-to-all, for head
+ * group `group`.  [OLMO] Eq. (96), [CP] "All-to-all", [HB] "Ulysses: transposing between
+ * the sequence and the heads": [B, S/C, H, D] per rank becomes [B, S, H/C, D] holding
+ * heads [g*H/C, (g+1)*H/C) for the whole sequence; sequence shard src supplies rows
+ * [src*S/C, (src+1)*S/C) (contiguous sharding).
+ *
+ *   CPATTN_SEQ_TO_HEADS: in  = the C rank shards stacked, [C][B][S/C][H][D]
+ *                        out = [B][S][H/C][D];
+ *                        out[b][src*S/C + i][h][d] = in[src][b][i][g*H/C + h][d]
+ *   CPATTN_HEADS_TO_SEQ: in  = [B][S][H/C][D], out = stacked [C][B][S/C][H][D]; writes
+ *                        only group g's heads of out (the rest is left untouched).
+ * Elements are opaque byte strings of elem_bytes (2 for bf16, 4 for fp32).  Bit-exact.
+ * Errors: INVALID_ARG (NULL pointer, sizes <= 0, bad dir, group outside [0, C), in == out),
+ * SHAPE (seq_len % C != 0 or heads % C != 0; C must divide the head count, [CP]
+ * "All-to-all" and [HB] "How to choose").
+ */
+cpattn_status_t cpattn_ulysses_permute(const void* in, void* out, int32_t elem_bytes,
+                                       int32_t batch, int64_t seq_len, int32_t heads,
+                                       int32_t head_dim, int32_t cp_size, int32_t group,
+                                       cpattn_permute_dir_t dir, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CPATTN_H */

@@ -1,0 +1,120 @@
+"""HIP block attention against the oracle element by element, on small seeded cases that
+span several tiles with ragged tails: both dtypes, grouped-query ratios, batch > 1, every
+zigzag step class (diagonal / entirely visible / entirely hidden), sparse positions, empty
+rows and empty key sets."""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import context_causal_attention_amd as cp
+import oracle
+from helpers import TOL, max_abs
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _inputs(seed, B, Sq, Skv, Hq, Hkv, D, dtype):
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn((B, Sq, Hq, D), generator=g).to(dtype)
+    k = torch.randn((B, Skv, Hkv, D), generator=g).to(dtype)
+    v = torch.randn((B, Skv, Hkv, D), generator=g).to(dtype)
+    return q, k, v
+
+
+def _run_and_compare(q, k, v, qpos, kvpos, scale, dtype_name):
+    out, lse = cp.block_fwd(q.to(DEV), k.to(DEV), v.to(DEV), torch.from_numpy(qpos).to(DEV),
+                            torch.from_numpy(kvpos).to(DEV), scale)
+    ref_o, ref_l = oracle.attention_rows(q.float().numpy(), k.float().numpy(), v.float().numpy(), qpos,
+                                         kvpos, scale)
+    o, l = out.cpu().numpy(), lse.cpu().numpy()
+    tol_o, tol_l = TOL[dtype_name]
+    eo, el = max_abs(o, ref_o), max_abs(l, ref_l)
+    assert eo <= tol_o and el <= tol_l, f"max abs err O {eo:.3g} lse {el:.3g}"
+    # rows with no visible key: exactly (0, -inf)
+    empty = np.isneginf(ref_l)
+    assert np.array_equal(np.isneginf(l), empty)
+    assert np.all(o.transpose(0, 2, 1, 3)[empty] == 0.0)
+    return eo, el
+
+
+CASES = [
+    # B, Sq, Skv, Hq, Hkv, D
+    (1, 256, 256, 2, 2, 128),
+    (2, 200, 333, 4, 2, 128),
+    (1, 130, 70, 8, 1, 128),
+    (1, 97, 300, 6, 2, 128),    # ratio 3: one query head per block row group
+    (1, 64, 128, 16, 2, 128),   # ratio 8: two head groups per K/V head
+    (1, 1, 1, 1, 1, 128),
+    (3, 45, 513, 4, 4, 128),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("case", CASES)
+def test_causal_contiguous(case, dtype):
+    B, Sq, Skv, Hq, Hkv, D = case
+    q, k, v = _inputs(hash(case) % 1000, B, Sq, Skv, Hq, Hkv, D, torch.bfloat16 if dtype == "bf16" else torch.float32)
+    # queries are the last Sq positions of a Skv-long sequence (a prefix-cache shape)
+    kvpos = np.arange(Skv, dtype=np.int64)
+    qpos = np.arange(Skv - Sq, Skv, dtype=np.int64) if Sq <= Skv else np.arange(Sq, dtype=np.int64)
+    _run_and_compare(q, k, v, qpos, kvpos, 1.0 / math.sqrt(D), dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("C,t", [(4, 96), (8, 40), (2, 200)])
+def test_zigzag_every_step_class(C, t, dtype):
+    """Rank r's local queries against every owner's shard: owner == r (diagonal chunks),
+    owner < r (early chunk fully visible), owner > r (early queries see nothing)."""
+    S = 2 * C * t
+    Hq, Hkv, D = 4, 2, 128
+    td = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q, _, _ = _inputs(C * t, 1, S // C, 1, Hq, Hkv, D, td)
+    for r in (0, C // 2, C - 1):
+        for o in range(C):
+            _, k, v = _inputs(1000 * o + r, 1, 1, S // C, Hq, Hkv, D, td)
+            _run_and_compare(q, k, v, oracle.zigzag_positions(S, C, r), oracle.zigzag_positions(S, C, o),
+                             0.088, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_sparse_positions_and_empty_rows(dtype):
+    rng = np.random.default_rng(5)
+    td = torch.bfloat16 if dtype == "bf16" else torch.float32
+    for trial in range(4):
+        Sq, Skv = int(rng.integers(1, 300)), int(rng.integers(1, 400))
+        qpos = np.sort(rng.choice(5000, Sq, replace=False)).astype(np.int64)
+        kvpos = np.sort(rng.choice(5000, Skv, replace=False)).astype(np.int64)
+        q, k, v = _inputs(trial, 2, Sq, Skv, 8, 2, 128, td)
+        _run_and_compare(q, k, v, qpos, kvpos, 0.1, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_all_hidden_and_no_keys(dtype):
+    td = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q, k, v = _inputs(9, 1, 100, 150, 4, 4, 128, td)
+    # every key later than every query: all rows empty
+    _run_and_compare(q, k, v, np.arange(100, dtype=np.int64), np.arange(1000, 1150, dtype=np.int64), 0.1, dtype)
+    # no keys at all
+    out, lse = cp.block_fwd(q.to(DEV), k[:, :0].contiguous().to(DEV), v[:, :0].contiguous().to(DEV),
+                            torch.arange(100, device=DEV), torch.zeros(0, dtype=torch.int64, device=DEV), 0.1)
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_fp32_head_dim_64():
+    q, k, v = _inputs(11, 2, 150, 150, 2, 1, 64, torch.float32)
+    pos = np.arange(150, dtype=np.int64)
+    _run_and_compare(q, k, v, pos, pos, 0.125, "fp32")
+
+
+def test_repeat_calls_are_identical():
+    """Same inputs, same outputs bit for bit (no dependence on scheduling)."""
+    q, k, v = _inputs(12, 1, 512, 512, 8, 2, 128, torch.bfloat16)
+    pos = torch.arange(512, device=DEV)
+    a = cp.block_fwd(q.to(DEV), k.to(DEV), v.to(DEV), pos, pos, 0.09)
+    b = cp.block_fwd(q.to(DEV), k.to(DEV), v.to(DEV), pos, pos, 0.09)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])

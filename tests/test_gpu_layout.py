@@ -1,0 +1,88 @@
+"""HIP layout kernels against the oracle, bit for bit: zigzag index, all-gather reorder,
+Ulysses permute (both directions), at small ragged shapes and at the workloads' sizes."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import context_causal_attention_amd as cp
+import oracle
+from context_causal_attention_amd.workloads import WORKLOADS
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.mark.parametrize("S,C", [(256, 4), (8192, 4), (32768, 4), (131072, 8), (262144, 8),
+                                 (48, 3), (2, 1), (64, 16), (1 << 20, 32)])
+def test_zigzag_index_bit_exact(S, C):
+    for r in range(C):
+        got = cp.zigzag_index(S, C, r, device=DEV).cpu().numpy()
+        assert np.array_equal(got, oracle.zigzag_positions(S, C, r)), (S, C, r)
+
+
+@pytest.mark.parametrize("C,t,B,row", [(4, 3, 2, 7), (4, 5, 1, 256), (8, 2, 3, 16), (3, 7, 2, 48),
+                                       (1, 4, 1, 32), (16, 1, 1, 5)])
+def test_reorder_bit_exact_small(C, t, B, row):
+    S = 2 * C * t
+    x = torch.randint(0, 256, (B, S, row), dtype=torch.uint8, generator=torch.Generator().manual_seed(C * t))
+    xd = x.to(DEV)
+    for direction in (cp.RANK_TO_SEQ, cp.SEQ_TO_RANK):
+        got = cp.reorder_gathered(xd, C, direction).cpu().numpy()
+        assert np.array_equal(got, oracle.reorder(x.numpy(), C, direction))
+    # round trip
+    back = cp.reorder_gathered(cp.reorder_gathered(xd, C, cp.RANK_TO_SEQ), C, cp.SEQ_TO_RANK)
+    assert torch.equal(back, xd)
+
+
+def test_reorder_bit_exact_allgather_32k():
+    w = WORKLOADS["allgather_32k"]
+    g = torch.Generator().manual_seed(3)
+    x = torch.randint(-32768, 32767, (w.batch, w.seq_len, w.heads_kv, w.head_dim), dtype=torch.int16,
+                      generator=g)  # bf16-sized rows of arbitrary bits
+    xd = x.to(DEV)
+    for direction in (cp.RANK_TO_SEQ, cp.SEQ_TO_RANK):
+        got = cp.reorder_gathered(xd, w.cp_size, direction).cpu().numpy()
+        assert np.array_equal(got, oracle.reorder(x.numpy(), w.cp_size, direction))
+
+
+@pytest.mark.parametrize("C,s,B,H,D,dt", [(4, 8, 1, 8, 16, torch.int16), (2, 3, 2, 4, 3, torch.int16),
+                                          (8, 5, 1, 8, 2, torch.int32), (4, 16, 2, 12, 128, torch.int16),
+                                          (3, 7, 1, 3, 5, torch.uint8)])
+def test_ulysses_bit_exact_small(C, s, B, H, D, dt):
+    g = torch.Generator().manual_seed(C * 100 + s)
+    lim = 127 if dt == torch.uint8 else 30000
+    lo = 0 if dt == torch.uint8 else -lim
+    stacked = torch.randint(lo, lim, (C, B, s, H, D), dtype=dt, generator=g)
+    sd = stacked.to(DEV)
+    back = torch.zeros_like(sd)
+    for grp in range(C):
+        got = cp.ulysses_seq_to_heads(sd, grp)
+        ref = oracle.ulysses_seq_to_heads(stacked.numpy(), C, grp)
+        assert np.array_equal(got.cpu().numpy(), ref)
+        cp.ulysses_heads_to_seq(got, grp, back)
+        ref_back = np.zeros_like(stacked.numpy())
+        oracle.ulysses_heads_to_seq(ref, C, grp, ref_back)
+        assert np.array_equal(back.cpu().numpy()[:, :, :, grp * (H // C):(grp + 1) * (H // C)],
+                              ref_back[:, :, :, grp * (H // C):(grp + 1) * (H // C)])
+    assert torch.equal(back, sd)
+
+
+def test_ulysses_bit_exact_gqa_128k():
+    """Q, K and V of one head group at S=131072 (32 Q / 8 KV heads, C=8), and the inverse
+    permute of the fp32 output into the stacked layout."""
+    w = WORKLOADS["ulysses_gqa_128k"]
+    C, grp, s = w.cp_size, w.group, w.seq_len // w.cp_size
+    g = torch.Generator().manual_seed(4)
+    for H in (w.heads_q, w.heads_kv):
+        stacked = torch.randint(-30000, 30000, (C, w.batch, s, H, w.head_dim), dtype=torch.int16, generator=g)
+        got = cp.ulysses_seq_to_heads(stacked.to(DEV), grp).cpu().numpy()
+        assert np.array_equal(got, oracle.ulysses_seq_to_heads(stacked.numpy(), C, grp))
+    grouped = torch.randn((w.batch, w.seq_len, w.heads_q // C, w.head_dim), generator=g)
+    out = torch.zeros((C, w.batch, s, w.heads_q, w.head_dim), device=DEV)
+    cp.ulysses_heads_to_seq(grouped.to(DEV), grp, out)
+    ref = np.zeros(tuple(out.shape), np.float32)
+    oracle.ulysses_heads_to_seq(grouped.numpy(), C, grp, ref)
+    assert np.array_equal(out.cpu().numpy(), ref)
