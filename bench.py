@@ -63,8 +63,9 @@ class Plan:
         self.kind = w.kind
         self.attn_flops = []   # FLOPs of each block attention launch of a step, in order
         if w.kind == "ring_share":
-            r = w.rank
-            self.q = synthetic.chunks("q", [r, 2 * C - 1 - r], heads=w.heads_q, **kw).to(dev)
+            # the rank's share, or every rank's share when the workload names no rank
+            self.ranks = [w.rank] if w.rank is not None else list(range(C))
+            self.qs = {r: synthetic.chunks("q", [r, 2 * C - 1 - r], heads=w.heads_q, **kw).to(dev) for r in self.ranks}
             self.k = [synthetic.chunks("k", [o, 2 * C - 1 - o], heads=w.heads_kv, **kw).to(dev) for o in range(C)]
             self.v = [synthetic.chunks("v", [o, 2 * C - 1 - o], heads=w.heads_kv, **kw).to(dev) for o in range(C)]
             self.pos = [torch.empty(w.local_len, dtype=torch.int64, device=dev) for _ in range(C)]
@@ -73,12 +74,11 @@ class Plan:
             self.tout = torch.empty_like(self.out)
             self.tlse = torch.empty_like(self.lse)
             t = w.chunk_len
-            for step in range(C):
-                owner = (r - step) % C
-                pairs = 2 * t * t + t if owner == r else 2 * t * t
-                self.attn_flops.append(4.0 * w.batch * w.heads_q * w.head_dim * pairs)
-            self.merge_bytes = (3 * self.out.numel() * 4 + 3 * self.lse.numel() * 4)
-            self.n_merge = C - 1
+            for r in self.ranks:
+                for step in range(C):
+                    owner = (r - step) % C
+                    pairs = 2 * t * t + t if owner == r else 2 * t * t
+                    self.attn_flops.append(4.0 * w.batch * w.heads_q * w.head_dim * pairs)
         elif w.kind == "allgather":
             gather = [c for rr in range(C) for c in (rr, 2 * C - 1 - rr)]
             self.kg = synthetic.chunks("k", gather, heads=w.heads_kv, **kw).to(dev)
@@ -135,16 +135,17 @@ class Plan:
                 cp.block_fwd(*a, **k)
 
         if self.kind == "ring_share":
-            r = w.rank
             for o in range(C):
                 cp.zigzag_index(w.seq_len, C, o, out=self.pos[o])
-            for step in range(C):
-                owner = (r - step) % C
-                if step == 0:
-                    attn(self.q, self.k[owner], self.v[owner], self.pos[r], self.pos[owner], w.scale, self.out, self.lse)
-                else:
-                    attn(self.q, self.k[owner], self.v[owner], self.pos[r], self.pos[owner], w.scale, self.tout, self.tlse)
-                    cp.lse_merge(self.out, self.lse, self.tout, self.tlse)
+            for r in self.ranks:
+                q = self.qs[r]
+                for step in range(C):
+                    owner = (r - step) % C
+                    if step == 0:
+                        attn(q, self.k[owner], self.v[owner], self.pos[r], self.pos[owner], w.scale, self.out, self.lse)
+                    else:
+                        attn(q, self.k[owner], self.v[owner], self.pos[r], self.pos[owner], w.scale, self.tout, self.tlse)
+                        cp.lse_merge(self.out, self.lse, self.tout, self.tlse)
         elif self.kind == "allgather":
             cp.reorder_gathered(self.kg, C, cp.RANK_TO_SEQ, out=self.kseq)
             cp.reorder_gathered(self.vg, C, cp.RANK_TO_SEQ, out=self.vseq)
@@ -181,7 +182,7 @@ def cpu_baseline(w, budget_s: float):
         qpos = np.arange(S, dtype=np.int64)
         heads = hq
     else:
-        r = w.rank if w.rank is not None else C - 1
+        r = w.rank if w.rank is not None else C - 1  # one rank stands for all: equal work per rank
         q = synthetic.chunks("q", [r, 2 * C - 1 - r], heads=w.heads_q, **kw).float().numpy()
         k = synthetic.chunks("k", range(2 * C), heads=w.heads_kv, **kw).float().numpy()
         v = synthetic.chunks("v", range(2 * C), heads=w.heads_kv, **kw).float().numpy()

@@ -7,24 +7,29 @@
 //   for each (b, query head h, local row i), over keys j of this block with
 //   kv_pos[j] <= q_pos[i]:  out_i = softmax_j(scale <q_i, k_j>) v_j,  lse_i = ln sum_j e^(s_ij).
 //
-// Work decomposition.  A block (256 threads = 4 waves) owns G query heads that share one
-// K/V head (G = 4, 2 or 1, whichever divides heads_q/heads_kv) times PQ = 128*NB/G query
-// positions.  Each wave owns NB "column blocks" of 32 query rows; every lane holds one
-// query row of each column block.
+// Work decomposition.  A block of NW waves owns G query heads that share one K/V head
+// (G = 4, 2 or 1, whichever divides heads_q/heads_kv) times PQ = 32*NW*NB/G query
+// positions.  Each wave owns NB column blocks of 32 query rows; every lane holds one query
+// row of each column block.  With NW = 8 two waves share a SIMD, so one wave's matrix
+// products overlap the other's softmax.
 //
 // Per K/V tile of 64 keys:
 //   S^T = K Q^T    with v_mfma_f32_32x32x16_bf16: A = 32 keys x 16 dims of K (LDS),
-//                  B = 16 dims x 32 queries of Q (registers, loaded once).
-//                  The accumulator gives each lane 16 keys of ONE query, so the row max and
-//                  row sum are lane-local plus one exchange with the other half-wave.
-//   online softmax in the log2 domain (scores pre-multiplied by scale*log2(e), exp2),
-//   P rounded to bf16 (RNE) straight from the accumulator registers,
+//                  B = 16 dims x 32 queries of Q (registers, loaded once).  The accumulator
+//                  gives each lane 16 keys of ONE query, so the row max is lane-local plus
+//                  one exchange with the other half-wave.
+//   softmax in the log2 domain (scores times scale*log2(e), exp2).  The running max is only
+//                  raised when a row's tile max exceeds it by more than kLazy (2^8 in weight):
+//                  the result is the same for any reference value, and skipping the raise
+//                  skips rescaling the accumulator.  Weights stay <= 2^8.
+//   P rounded to bf16 (RNE) straight from the accumulator registers; the row sum adds the
+//                  fp32 weights (rounding them first would cost lse up to 2^-9 on short rows).
 //   O^T += V^T P^T with A = 32 dims x 16 keys of V read transposed from the row-major LDS
 //                  tile by ds_read_b64_tr_b16, B = P^T (registers).  The key order inside a
 //                  16-key step is the accumulator's own order, applied to V's addresses.
-// K and V tiles are double-buffered in LDS (XOR-swizzled 16-byte chunks, conflict-free
-// for both the row reads of K and the transposed reads of V); the next tile's global loads
-// are in flight while the current tile is computed.
+// K and V tiles go from global memory straight into LDS (global_load_lds_dwordx4; each lane
+// lands 16 bytes at base + 16*lane, so the XOR-swizzled layout is chosen by which chunk each
+// lane fetches).  Two LDS stages: the next tile is in flight while the current one is used.
 //
 // Causal skip ("Context parallelism: Ring Attention and Ulysses", Ring Attention: blocks
 // later than the query are skipped whole): with strictly increasing positions the visible
@@ -45,15 +50,15 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_AS __attribute__((address_space(3)))
+#define GLOBAL_AS __attribute__((address_space(1)))
 
 constexpr int kD = 128;             // head dim
 constexpr int kBN = 64;             // keys per tile
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
 constexpr int kRowBytes = kD * 2;   // one K/V row in LDS
 constexpr int kTileBytes = kBN * kRowBytes;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazy = 8.0f;       // raise the running max only past this margin (log2)
 
 struct Params {
     const __bf16* q;
@@ -83,8 +88,8 @@ __device__ inline int wave_sum(int x) {
     return x;
 }
 
-// Value of the other half-wave (lane ^ 32) combined with our own: both outputs of the
-// half-swap hold {ours, theirs}.
+// Combine a value with the other half-wave's (lane ^ 32): both outputs of the half-swap
+// hold {ours, theirs}.
 __device__ inline float half_max(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -110,11 +115,22 @@ __device__ inline bf16x8 pack_bf16(const f32x16& s, int base) {
     return r;
 }
 
-template <int NB>
-__global__ void __launch_bounds__(kThreads, 1) block_fwd_bf16_kernel(const Params p) {
-    __shared__ __attribute__((aligned(16))) char lds_raw[4 * kTileBytes];  // [buf][K|V][tile]
-    __shared__ int red[2 * kWaves];
-    LDS_AS char* lds = (LDS_AS char*)lds_raw;
+// One 16-byte direct global->LDS load: this lane's 16 bytes land at lds_base + 16*lane.
+__device__ inline void load_lds16(const void* g, LDS_AS void* lds_base) {
+    __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)g, lds_base, 16, 0, 0);
+}
+
+template <int NW, int NB>
+__global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params p) {
+    constexpr int kThreads = 64 * NW;
+    // K/V tile row r, 16-byte chunk c is stored at chunk c ^ swz(r):
+    //   K: r & 15 (row reads by 16 consecutive keys are conflict-free)
+    //   V: (r & 7) << 1 (transposed reads of 4 consecutive keys are conflict-free)
+    // two stages in two distinct arrays, so that the compiler can tell the stage being read
+    // from the stage being filled and does not wait for the fill before reading
+    __shared__ __attribute__((aligned(16))) char lds_stage0[2 * kTileBytes];  // [K|V][tile]
+    __shared__ __attribute__((aligned(16))) char lds_stage1[2 * kTileBytes];
+    __shared__ int red[2 * NW];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -158,15 +174,41 @@ __global__ void __launch_bounds__(kThreads, 1) block_fwd_bf16_kernel(const Param
     c_full = wave_sum(c_full);
     if (lane == 0) {
         red[w] = c_ne;
-        red[kWaves + w] = c_full;
+        red[NW + w] = c_full;
     }
     __syncthreads();
     int n_ne = 0, n_full = 0;
 #pragma unroll
-    for (int i = 0; i < kWaves; ++i) {
+    for (int i = 0; i < NW; ++i) {
         n_ne += red[i];
-        n_full += red[kWaves + i];
+        n_full += red[NW + i];
     }
+
+    // ---- K/V tile loads: each wave fills (64 / NW) rows of K and of V per tile, four rows
+    // (1 KB) per instruction; lane -> row (lane >> 4), stored chunk (lane & 15)
+    const int64_t kvstride = (int64_t)p.heads_kv * kD;  // elements between consecutive keys
+    const __bf16* kbase = p.k + (b * p.seq_kv * p.heads_kv + kvh) * (int64_t)kD;
+    const __bf16* vbase = p.v + (b * p.seq_kv * p.heads_kv + kvh) * (int64_t)kD;
+    constexpr int kRowsPerWave = kBN / NW;
+    constexpr int kLoadsPerWave = kRowsPerWave / 4;
+    const int ld_row_in = lane >> 4;   // row within the 4-row slab
+    const int ld_chunk = lane & 15;    // stored chunk
+    auto issue_tile = [&](int jt, LDS_AS char* kt) {
+        LDS_AS char* vt = kt + kTileBytes;
+#pragma unroll
+        for (int i = 0; i < kLoadsPerWave; ++i) {
+            const int row = w * kRowsPerWave + 4 * i + ld_row_in;
+            int64_t j = (int64_t)jt * kBN + row;
+            // rows past the end read the last key (finite data); the mask hides them
+            if (j >= p.seq_kv) j = p.seq_kv - 1;
+            const int kc = ld_chunk ^ (row & 15);
+            const int vc = ld_chunk ^ ((row & 7) << 1);
+            LDS_AS char* slab_k = kt + (w * kRowsPerWave + 4 * i) * kRowBytes;
+            LDS_AS char* slab_v = vt + (w * kRowsPerWave + 4 * i) * kRowBytes;
+            load_lds16(kbase + j * kvstride + kc * 8, slab_k);
+            load_lds16(vbase + j * kvstride + vc * 8, slab_v);
+        }
+    };
 
     // ---- this lane's query rows; Q as MFMA B operands (16 dims x 32 queries per step)
     bf16x8 qreg[NB][kD / 16];
@@ -201,15 +243,14 @@ __global__ void __launch_bounds__(kThreads, 1) block_fwd_bf16_kernel(const Param
         for (int db = 0; db < kD / 32; ++db) acc_o[nb][db] = f32x16{};
     }
 
-    // ---- per-lane LDS offsets
-    // K (row reads): key = 32*kb + l32, 16-byte chunk (2*ks + half) XOR (key & 15)
+    // ---- per-lane LDS read offsets
+    // K (row reads): key = 32*kb + l32, chunk (2*ks + half) stored at chunk ^ (key & 15)
     uint32_t off_k[kD / 16];
 #pragma unroll
     for (int ks = 0; ks < kD / 16; ++ks)
         off_k[ks] = l32 * kRowBytes + (((2 * ks + half) ^ (lane & 15)) << 4);
     // V (transposed reads): in each 16-lane group, lane s reads 4 dims starting at
-    // 16*(group&1) + 4*(s&3) of key (s>>2) + 4*half (+8 for the second read);
-    // chunk XOR ((key & 7) << 1)
+    // 16*(group&1) + 4*(s&3) of key (s>>2) + 4*half (+8 for the second read)
     const int grp = lane >> 4, s16 = lane & 15;
     const int vkey = 4 * half + (s16 >> 2);
     const int vsw = (vkey & 7) << 1;
@@ -220,51 +261,13 @@ __global__ void __launch_bounds__(kThreads, 1) block_fwd_bf16_kernel(const Param
         off_v[db] = vkey * kRowBytes + ((chunk ^ vsw) << 4) + ((s16 & 1) << 3);
     }
 
-    // ---- global -> register staging of one K/V tile: thread owns 16-byte chunk (tid & 15)
-    // of keys 16*i + (tid >> 4), i = 0..3, for K and V
-    const __bf16* kbase = p.k + (b * p.seq_kv * p.heads_kv + kvh) * (int64_t)kD;
-    const __bf16* vbase = p.v + (b * p.seq_kv * p.heads_kv + kvh) * (int64_t)kD;
-    const int64_t kstride = (int64_t)p.heads_kv * kD;
-    const int st_chunk = tid & 15;
-    const int st_key = tid >> 4;
-    u32x4 stage_k[4], stage_v[4];
+    LDS_AS char* st0 = (LDS_AS char*)lds_stage0;
+    LDS_AS char* st1 = (LDS_AS char*)lds_stage1;
 
-    auto load_tile = [&](int jt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t j = (int64_t)jt * kBN + 16 * i + st_key;
-            if (j < p.seq_kv) {
-                stage_k[i] = *(const u32x4*)(kbase + j * kstride + st_chunk * 8);
-                stage_v[i] = *(const u32x4*)(vbase + j * kstride + st_chunk * 8);
-            } else {
-                stage_k[i] = u32x4{0, 0, 0, 0};
-                stage_v[i] = u32x4{0, 0, 0, 0};
-            }
-        }
-    };
-    auto store_tile = [&](int buf) {
-        LDS_AS char* kt = lds + buf * 2 * kTileBytes;
-        LDS_AS char* vt = kt + kTileBytes;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int key = 16 * i + st_key;
-            *(LDS_AS u32x4*)(kt + key * kRowBytes + ((st_chunk ^ (key & 15)) << 4)) = stage_k[i];
-            *(LDS_AS u32x4*)(vt + key * kRowBytes + ((st_chunk ^ ((key & 7) << 1)) << 4)) = stage_v[i];
-        }
-    };
-
-    if (n_ne > 0) {
-        load_tile(0);
-        store_tile(0);
-    }
-    __syncthreads();
-
-    for (int jt = 0; jt < n_ne; ++jt) {
-        const int buf = jt & 1;
-        const bool more = jt + 1 < n_ne;
-        if (more) load_tile(jt + 1);
-        const LDS_AS char* kt = lds + buf * 2 * kTileBytes;
+    // one tile: prefetch tile jt+1 into `nxt`, compute tile jt from `cur`
+    auto tile = [&](int jt, const LDS_AS char* kt, LDS_AS char* nxt) {
         const LDS_AS char* vt = kt + kTileBytes;
+        if (jt + 1 < n_ne) issue_tile(jt + 1, nxt);
 
         // S^T = K Q^T
         f32x16 s[NB][2];
@@ -290,17 +293,21 @@ __global__ void __launch_bounds__(kThreads, 1) block_fwd_bf16_kernel(const Param
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-                for (int vv = 0; vv < 16; ++vv) {
-                    const int64_t j = (int64_t)jt * kBN + 32 * kb + 8 * (vv >> 2) + 4 * half + (vv & 3);
-                    const int64_t kp = (j < p.seq_kv) ? p.kvpos[j] : INT64_MAX;
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int64_t j0 = (int64_t)jt * kBN + 32 * kb + 8 * g4 + 4 * half;
 #pragma unroll
-                    for (int nb = 0; nb < NB; ++nb)
-                        if (kp > mypos[nb]) s[nb][kb][vv] = -INFINITY;
+                    for (int e = 0; e < 4; ++e) {
+                        const int64_t j = j0 + e;
+                        const int64_t kp = (j < p.seq_kv) ? p.kvpos[j] : INT64_MAX;
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb)
+                            if (kp > mypos[nb]) s[nb][kb][4 * g4 + e] = -INFINITY;
+                    }
                 }
             }
         }
 
-        // online softmax, log2 domain; P^T as MFMA B operands straight from registers
+        // softmax, log2 domain, lazy raise of the running max
         bf16x8 pb[NB][2][2];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
@@ -309,11 +316,19 @@ __global__ void __launch_bounds__(kThreads, 1) block_fwd_bf16_kernel(const Param
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int vv = 0; vv < 16; ++vv) mx = fmaxf(mx, s[nb][kb][vv]);
-            mx = half_max(mx);
-            const float m_new = fmaxf(m_run[nb], mx * p.c);
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m_run[nb] - m_use);
-            float rs = 0.f;
+            const float mt = half_max(mx) * p.c;
+            // raise only when some row of the wave gained more than kLazy (wave-uniform)
+            if (__builtin_amdgcn_ballot_w64(mt > m_run[nb] + kLazy) != 0) {
+                const float m_new = fmaxf(m_run[nb], mt);
+                const float m_new_use = (m_new == -INFINITY) ? 0.f : m_new;
+                const float alpha = __builtin_amdgcn_exp2f(m_run[nb] - m_new_use);
+                l_run[nb] *= alpha;
+#pragma unroll
+                for (int db = 0; db < kD / 32; ++db) acc_o[nb][db] *= alpha;
+                m_run[nb] = m_new;
+            }
+            const float m_use = (m_run[nb] == -INFINITY) ? 0.f : m_run[nb];
+            float rs = l_run[nb];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -322,10 +337,7 @@ __global__ void __launch_bounds__(kThreads, 1) block_fwd_bf16_kernel(const Param
                     s[nb][kb][vv] = e;
                     rs += e;
                 }
-            l_run[nb] = l_run[nb] * alpha + rs;
-            m_run[nb] = m_new;
-#pragma unroll
-            for (int db = 0; db < kD / 32; ++db) acc_o[nb][db] *= alpha;
+            l_run[nb] = rs;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 pb[nb][kb][0] = pack_bf16(s[nb][kb], 0);
@@ -349,8 +361,17 @@ __global__ void __launch_bounds__(kThreads, 1) block_fwd_bf16_kernel(const Param
             }
         }
 
-        if (more) store_tile(buf ^ 1);
+        // the next tile has landed in LDS (own loads) and every wave is done with this one
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
+    };
+
+    if (n_ne > 0) issue_tile(0, st0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int jt = 0; jt < n_ne; jt += 2) {
+        tile(jt, st0, st1);
+        if (jt + 1 < n_ne) tile(jt + 1, st1, st0);
     }
 
     // ---- epilogue: combine the half-wave row sums, normalise, store
@@ -378,6 +399,15 @@ __global__ void __launch_bounds__(kThreads, 1) block_fwd_bf16_kernel(const Param
     }
 }
 
+template <int NW, int NB>
+hipError_t launch_variant(Params p, int64_t seq_q, hipStream_t stream) {
+    p.pq = 32 * NW * NB / p.G;
+    p.n_qt = (seq_q + p.pq - 1) / p.pq;
+    const int64_t blocks = p.n_qt * p.n_cols;
+    hipLaunchKernelGGL((block_fwd_bf16_kernel<NW, NB>), dim3((unsigned)blocks), dim3(64 * NW), 0, stream, p);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_block_fwd_bf16(const BlockFwdArgs& a, hipStream_t stream) {
@@ -399,21 +429,13 @@ hipError_t launch_block_fwd_bf16(const BlockFwdArgs& a, hipStream_t stream) {
     p.n_cols = a.batch * a.heads_kv * p.n_hg;
     p.xcd_cols = (p.n_cols % 8 == 0) ? p.n_cols / 8 : 0;
     p.c = a.scale * kLog2e;
-    // two column blocks per wave unless that leaves the chip less than half full
-    int nb = 2;
-    {
-        const int64_t pq2 = 128 * 2 / p.G;
-        const int64_t blocks2 = ((a.seq_q + pq2 - 1) / pq2) * p.n_cols;
-        if (blocks2 < 512) nb = 1;
-    }
-    p.pq = 128 * nb / p.G;
-    p.n_qt = (a.seq_q + p.pq - 1) / p.pq;
-    const int64_t blocks = p.n_qt * p.n_cols;
-    if (nb == 2)
-        hipLaunchKernelGGL(block_fwd_bf16_kernel<2>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
-    else
-        hipLaunchKernelGGL(block_fwd_bf16_kernel<1>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
-    return hipGetLastError();
+    // 8 waves x 32 rows per block; 4 waves x 32 rows when that would leave the chip less
+    // than half full
+    const int64_t rows = a.seq_q * (int64_t)p.G;
+    const int64_t blocks8 = ((a.seq_q + 256 / p.G - 1) / (256 / p.G)) * p.n_cols;
+    (void)rows;
+    if (blocks8 < 512) return launch_variant<4, 1>(p, a.seq_q, stream);
+    return launch_variant<8, 1>(p, a.seq_q, stream);
 }
 
 }  // namespace cpattn
