@@ -45,6 +45,9 @@ def parse_args(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="before the steps, run one plain chunk copy (reorder_gathered) of this "
+                         "many MiB, as the reference dispatch for hardware byte counters")
     return ap.parse_args(argv)
 
 
@@ -161,6 +164,24 @@ class Plan:
             cp.ulysses_heads_to_seq(self.og, g, self.ost)
 
 
+def profiled_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of ``kernel`` from the committed rocprofv3 counter summary of
+    this workload, or None when there is none or the kernel source changed since."""
+    import hashlib
+    f = ROOT / "profiles" / f"block_fwd_bf16_{workload}_traffic.txt"
+    src = ROOT / "context_causal_attention_amd" / "csrc" / "block_fwd_bf16.hip"
+    if not f.exists() or not src.exists():
+        return None
+    sha = hashlib.sha256(src.read_bytes()).hexdigest()[:16]
+    recorded, value = None, None
+    for line in f.read_text().splitlines():
+        if line.startswith("kernel_source:"):
+            recorded = line.split()[-1]
+        if line.startswith(f"traffic_bytes_per_launch {kernel}:"):
+            value = float(line.split()[-1])
+    return value if recorded == sha else None
+
+
 def cpu_baseline(w, budget_s: float):
     """The CPU oracle (as it stands) on a bounded sample of the same workload: direct causal
     attention of a seeded sample of the share's query rows, all heads, fp64."""
@@ -225,6 +246,13 @@ def main(argv=None) -> int:
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     plan = Plan(w, dev)
+    if args.copy_calibration_mib > 0:
+        import context_causal_attention_amd as cp
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).view(1, 64, n // 64)
+        src.fill_(1)
+        cp.reorder_gathered(src, 4, cp.RANK_TO_SEQ)  # reads n bytes, writes n bytes
+        del src
     torch.cuda.synchronize()
     for _ in range(args.warmup):
         plan.step()
@@ -262,7 +290,8 @@ def main(argv=None) -> int:
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "kernel": "block_fwd_bf16_kernel" if w.dtype == "bf16" else "block_fwd_f32_kernel",
                      "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "frac": round(achieved / peak, 4),
+                     "traffic": profiled_traffic(w.name, "block_fwd_bf16_kernel") if w.dtype == "bf16" else None,
                      "avg_launch_ms": round(sum(attn_ms) / len(attn_ms), 4), "launches": len(attn_ms)},
     }
     if not args.no_cpu_baseline:
