@@ -120,12 +120,18 @@ __device__ inline void load_lds16(const void* g, LDS_AS void* lds_base) {
     __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)g, lds_base, 16, 0, 0);
 }
 
+// LDS operand reads kept in flight ahead of the matrix products (K: one read per MFMA,
+// V: two transposed reads per MFMA)
+constexpr int kReadAheadK = 4;
+constexpr int kReadAheadV = 2;
+
 template <int NW, int NB>
 __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params p) {
     constexpr int kThreads = 64 * NW;
     // K/V tile row r, 16-byte chunk c is stored at chunk c ^ swz(r):
     //   K: r & 15 (row reads by 16 consecutive keys are conflict-free)
-    //   V: (r & 7) << 1 (transposed reads of 4 consecutive keys are conflict-free)
+    //   V: (r & 3) << 2 (transposed reads: each 32-lane half reads 4 consecutive keys x 64 B,
+    //      which this spreads over all 64 banks)
     // two stages in two distinct arrays, so that the compiler can tell the stage being read
     // from the stage being filled and does not wait for the fill before reading
     __shared__ __attribute__((aligned(16))) char lds_stage0[2 * kTileBytes];  // [K|V][tile]
@@ -185,28 +191,43 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
     }
 
     // ---- K/V tile loads: each wave fills (64 / NW) rows of K and of V per tile, four rows
-    // (1 KB) per instruction; lane -> row (lane >> 4), stored chunk (lane & 15)
+    // (1 KB) per instruction; lane -> row (lane >> 4), stored chunk (lane & 15).  The source
+    // address is a wave-uniform tile base plus a per-lane byte offset fixed for the kernel;
+    // only a ragged last tile clamps its rows (to the last key, finite data the mask hides).
     const int64_t kvstride = (int64_t)p.heads_kv * kD;  // elements between consecutive keys
-    const __bf16* kbase = p.k + (b * p.seq_kv * p.heads_kv + kvh) * (int64_t)kD;
-    const __bf16* vbase = p.v + (b * p.seq_kv * p.heads_kv + kvh) * (int64_t)kD;
+    const char* kbase = (const char*)(p.k + (b * p.seq_kv * p.heads_kv + kvh) * (int64_t)kD);
+    const char* vbase = (const char*)(p.v + (b * p.seq_kv * p.heads_kv + kvh) * (int64_t)kD);
+    const int64_t tile_bytes_g = (int64_t)kBN * kvstride * 2;  // global bytes between tiles
     constexpr int kRowsPerWave = kBN / NW;
     constexpr int kLoadsPerWave = kRowsPerWave / 4;
     const int ld_row_in = lane >> 4;   // row within the 4-row slab
     const int ld_chunk = lane & 15;    // stored chunk
+    uint32_t koff[kLoadsPerWave], voff[kLoadsPerWave];
+#pragma unroll
+    for (int i = 0; i < kLoadsPerWave; ++i) {
+        const int row = w * kRowsPerWave + 4 * i + ld_row_in;
+        koff[i] = (uint32_t)(row * kvstride * 2) + ((ld_chunk ^ (row & 15)) << 4);
+        voff[i] = (uint32_t)(row * kvstride * 2) + ((ld_chunk ^ ((row & 3) << 2)) << 4);
+    }
     auto issue_tile = [&](int jt, LDS_AS char* kt) {
         LDS_AS char* vt = kt + kTileBytes;
+        const char* kb_t = kbase + (int64_t)jt * tile_bytes_g;
+        const char* vb_t = vbase + (int64_t)jt * tile_bytes_g;
+        if ((int64_t)(jt + 1) * kBN <= p.seq_kv) {
 #pragma unroll
-        for (int i = 0; i < kLoadsPerWave; ++i) {
-            const int row = w * kRowsPerWave + 4 * i + ld_row_in;
-            int64_t j = (int64_t)jt * kBN + row;
-            // rows past the end read the last key (finite data); the mask hides them
-            if (j >= p.seq_kv) j = p.seq_kv - 1;
-            const int kc = ld_chunk ^ (row & 15);
-            const int vc = ld_chunk ^ ((row & 7) << 1);
-            LDS_AS char* slab_k = kt + (w * kRowsPerWave + 4 * i) * kRowBytes;
-            LDS_AS char* slab_v = vt + (w * kRowsPerWave + 4 * i) * kRowBytes;
-            load_lds16(kbase + j * kvstride + kc * 8, slab_k);
-            load_lds16(vbase + j * kvstride + vc * 8, slab_v);
+            for (int i = 0; i < kLoadsPerWave; ++i) {
+                load_lds16(kb_t + koff[i], kt + (w * kRowsPerWave + 4 * i) * kRowBytes);
+                load_lds16(vb_t + voff[i], vt + (w * kRowsPerWave + 4 * i) * kRowBytes);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < kLoadsPerWave; ++i) {
+                const int row = w * kRowsPerWave + 4 * i + ld_row_in;
+                const int64_t j = (int64_t)jt * kBN + row;
+                const int64_t over = (j >= p.seq_kv) ? (j - (p.seq_kv - 1)) * kvstride * 2 : 0;
+                load_lds16(kb_t + koff[i] - over, kt + (w * kRowsPerWave + 4 * i) * kRowBytes);
+                load_lds16(vb_t + voff[i] - over, vt + (w * kRowsPerWave + 4 * i) * kRowBytes);
+            }
         }
     };
 
@@ -253,7 +274,7 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
     // 16*(group&1) + 4*(s&3) of key (s>>2) + 4*half (+8 for the second read)
     const int grp = lane >> 4, s16 = lane & 15;
     const int vkey = 4 * half + (s16 >> 2);
-    const int vsw = (vkey & 7) << 1;
+    const int vsw = (vkey & 3) << 2;
     uint32_t off_v[kD / 32];
 #pragma unroll
     for (int db = 0; db < kD / 32; ++db) {
@@ -286,6 +307,14 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
                     s[nb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[nb][ks], s[nb][kb], 0, 0, 0);
             }
         }
+        // keep the operand reads kReadAheadK ahead of the matrix products
+        __builtin_amdgcn_sched_group_barrier(0x100, kReadAheadK, 1);
+#pragma unroll
+        for (int i = 0; i < 16 - kReadAheadK; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, NB, 1);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, NB * kReadAheadK, 1);
 
         // element mask on tiles not entirely visible: key index of accumulator entry v is
         // 32*kb + 8*(v/4) + 4*half + v%4
@@ -360,14 +389,21 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
                 }
             }
         }
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * kReadAheadV, 2);
+#pragma unroll
+        for (int i = 0; i < 16 - kReadAheadV; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, NB, 2);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, NB * kReadAheadV, 2);
 
         // the next tile has landed in LDS (own loads) and every wave is done with this one
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), visible to the compiler
         __syncthreads();
     };
 
     if (n_ne > 0) issue_tile(0, st0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), visible to the compiler
     __syncthreads();
     for (int jt = 0; jt < n_ne; jt += 2) {
         tile(jt, st0, st1);
@@ -431,9 +467,7 @@ hipError_t launch_block_fwd_bf16(const BlockFwdArgs& a, hipStream_t stream) {
     p.c = a.scale * kLog2e;
     // 8 waves x 32 rows per block; 4 waves x 32 rows when that would leave the chip less
     // than half full
-    const int64_t rows = a.seq_q * (int64_t)p.G;
     const int64_t blocks8 = ((a.seq_q + 256 / p.G - 1) / (256 / p.G)) * p.n_cols;
-    (void)rows;
     if (blocks8 < 512) return launch_variant<4, 1>(p, a.seq_q, stream);
     return launch_variant<8, 1>(p, a.seq_q, stream);
 }
