@@ -7,7 +7,8 @@ A step is one pass of the whole hot path over one batch of synthetic input alrea
 in HBM.  For the default workload (ring_share_256k: S=262144, C=8 zigzag, rank 3, 32 query /
 8 KV heads, D=128, bf16) that is: the zigzag positions of every owner, then for each of the
 8 ring steps one block attention of the rank's 32768 local queries against the owner's
-32768-token K/V shard, folded into the accumulator by the LSE merge (7 merges).
+32768-token K/V shard; steps 1..7 fold their result into the accumulator by the LSE merge in
+the attention kernel's epilogue (``--unfused``: a separate merge kernel after each step).
 
 The value is whole-job throughput in TFLOP/s counting unmasked FLOPs only: 4*D FLOPs per
 visible (query, key) pair and query head (two matrix products; softmax not counted).
@@ -43,6 +44,8 @@ def parse_args(argv=None):
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="ring_share_256k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--unfused", action="store_true",
+                    help="ring share: write each step's tile and merge it with the separate merge kernel")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -54,7 +57,7 @@ def parse_args(argv=None):
 class Plan:
     """Buffers and the launch sequence of one step of a workload."""
 
-    def __init__(self, w, dev):
+    def __init__(self, w, dev, fused=True):
         import torch
         import context_causal_attention_amd as cp
         from context_causal_attention_amd import synthetic
@@ -64,6 +67,7 @@ class Plan:
         kw = dict(batch=w.batch, chunk_len=w.chunk_len, head_dim=w.head_dim, dtype=td)
         C = w.cp_size
         self.kind = w.kind
+        self.fused = fused
         self.attn_flops = []   # FLOPs of each block attention launch of a step, in order
         if w.kind == "ring_share":
             # the rank's share, or every rank's share when the workload names no rank
@@ -74,8 +78,9 @@ class Plan:
             self.pos = [torch.empty(w.local_len, dtype=torch.int64, device=dev) for _ in range(C)]
             self.out = torch.empty((w.batch, w.local_len, w.heads_q, w.head_dim), dtype=torch.float32, device=dev)
             self.lse = torch.empty((w.batch, w.heads_q, w.local_len), dtype=torch.float32, device=dev)
-            self.tout = torch.empty_like(self.out)
-            self.tlse = torch.empty_like(self.lse)
+            if not fused:
+                self.tout = torch.empty_like(self.out)
+                self.tlse = torch.empty_like(self.lse)
             t = w.chunk_len
             for r in self.ranks:
                 for step in range(C):
@@ -127,15 +132,15 @@ class Plan:
         cp, torch, w = self.cp, self.torch, self.w
         C = w.cp_size
 
-        def attn(*a, **k):
+        def attn(*a, fn=cp.block_fwd):
             if ev is not None:
                 s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 s.record()
-                cp.block_fwd(*a, **k)
+                fn(*a)
                 e.record()
                 ev.append((s, e))
             else:
-                cp.block_fwd(*a, **k)
+                fn(*a)
 
         if self.kind == "ring_share":
             for o in range(C):
@@ -144,10 +149,13 @@ class Plan:
                 q = self.qs[r]
                 for step in range(C):
                     owner = (r - step) % C
+                    a = (q, self.k[owner], self.v[owner], self.pos[r], self.pos[owner], w.scale)
                     if step == 0:
-                        attn(q, self.k[owner], self.v[owner], self.pos[r], self.pos[owner], w.scale, self.out, self.lse)
+                        attn(*a, self.out, self.lse)
+                    elif self.fused:
+                        attn(*a, self.out, self.lse, fn=cp.block_fwd_merge)
                     else:
-                        attn(q, self.k[owner], self.v[owner], self.pos[r], self.pos[owner], w.scale, self.tout, self.tlse)
+                        attn(*a, self.tout, self.tlse)
                         cp.lse_merge(self.out, self.lse, self.tout, self.tlse)
         elif self.kind == "allgather":
             cp.reorder_gathered(self.kg, C, cp.RANK_TO_SEQ, out=self.kseq)
@@ -245,7 +253,7 @@ def main(argv=None) -> int:
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    plan = Plan(w, dev)
+    plan = Plan(w, dev, fused=not args.unfused)
     if args.copy_calibration_mib > 0:
         import context_causal_attention_amd as cp
         n = args.copy_calibration_mib << 20
@@ -284,7 +292,8 @@ def main(argv=None) -> int:
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic (seeded iid N(0,1), per-chunk generators)",
-        "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seq_len, "cp_size": w.cp_size,
+        "config": {"workload": w.name + ("_unfused" if args.unfused and w.kind == "ring_share" else ""),
+                   "batch": w.batch, "seq_len": w.seq_len, "cp_size": w.cp_size,
                    "rank": w.rank, "group": w.group, "heads_q": w.heads_q, "heads_kv": w.heads_kv,
                    "head_dim": w.head_dim, "unmasked_flops_per_step": plan.flops},
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),

@@ -12,6 +12,7 @@ from ._binding import (  # noqa: F401
     SEQ_TO_RANK,
     CpattnError,
     block_fwd,
+    block_fwd_merge,
     header_entry_points,
     library_path,
     load_library,

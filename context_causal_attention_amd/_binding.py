@@ -53,10 +53,11 @@ def load_library():
     L.cpattn_abi_version.restype = i32
     L.cpattn_zigzag_index.argtypes = [i64, i32, i32, P, P]
     L.cpattn_block_fwd.argtypes = [P, P, P, ctypes.c_int, i32, i64, i64, i32, i32, i32, P, P, f32, P, P, P]
+    L.cpattn_block_fwd_merge.argtypes = list(L.cpattn_block_fwd.argtypes)
     L.cpattn_lse_merge.argtypes = [P, P, P, P, i32, i64, i32, i32, P]
     L.cpattn_reorder_gathered.argtypes = [P, P, i32, i64, i64, i32, ctypes.c_int, P]
     L.cpattn_ulysses_permute.argtypes = [P, P, i32, i32, i64, i32, i32, i32, i32, ctypes.c_int, P]
-    for name in ("cpattn_zigzag_index", "cpattn_block_fwd", "cpattn_lse_merge",
+    for name in ("cpattn_zigzag_index", "cpattn_block_fwd", "cpattn_block_fwd_merge", "cpattn_lse_merge",
                  "cpattn_reorder_gathered", "cpattn_ulysses_permute"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
@@ -108,14 +109,7 @@ def zigzag_index(seq_len: int, cp_size: int, rank: int, out: torch.Tensor | None
     return out
 
 
-def block_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_pos: torch.Tensor,
-              kv_pos: torch.Tensor, scale: float, out: torch.Tensor | None = None,
-              lse: torch.Tensor | None = None):
-    """One block of causal attention on global positions.
-
-    q [B, Sq, Hq, D]; k, v [B, Skv, Hkv, D] (both bf16 or both fp32); positions int64.
-    Returns (out fp32 [B, Sq, Hq, D], lse fp32 [B, Hq, Sq]).
-    """
+def _block_fwd_call(entry: str, q, k, v, q_pos, kv_pos, scale, out, lse, alloc: bool):
     L = load_library()
     if q.dtype not in (torch.bfloat16, torch.float32):
         raise ValueError("q must be bf16 or fp32")
@@ -126,16 +120,35 @@ def block_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_pos: torch.Te
     _need(v, "v", q.dtype, (B, Skv, Hkv, D))
     _need(q_pos, "q_pos", torch.int64, (Sq,))
     _need(kv_pos, "kv_pos", torch.int64, (Skv,))
-    if out is None:
+    if alloc and out is None:
         out = torch.empty((B, Sq, Hq, D), dtype=torch.float32, device=q.device)
-    if lse is None:
+    if alloc and lse is None:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
     _need(out, "out", torch.float32, (B, Sq, Hq, D))
     _need(lse, "lse", torch.float32, (B, Hq, Sq))
     dt = CPATTN_BF16 if q.dtype == torch.bfloat16 else CPATTN_F32
-    _check(L.cpattn_block_fwd(_ptr(q), _ptr(k), _ptr(v), dt, B, Sq, Skv, Hq, Hkv, D, _ptr(q_pos),
-                              _ptr(kv_pos), float(scale), _ptr(out), _ptr(lse), _stream(q.device)))
+    _check(getattr(L, entry)(_ptr(q), _ptr(k), _ptr(v), dt, B, Sq, Skv, Hq, Hkv, D, _ptr(q_pos),
+                             _ptr(kv_pos), float(scale), _ptr(out), _ptr(lse), _stream(q.device)))
     return out, lse
+
+
+def block_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_pos: torch.Tensor,
+              kv_pos: torch.Tensor, scale: float, out: torch.Tensor | None = None,
+              lse: torch.Tensor | None = None):
+    """One block of causal attention on global positions.
+
+    q [B, Sq, Hq, D]; k, v [B, Skv, Hkv, D] (both bf16 or both fp32); positions int64.
+    Returns (out fp32 [B, Sq, Hq, D], lse fp32 [B, Hq, Sq]).
+    """
+    return _block_fwd_call("cpattn_block_fwd", q, k, v, q_pos, kv_pos, scale, out, lse, alloc=True)
+
+
+def block_fwd_merge(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_pos: torch.Tensor,
+                    kv_pos: torch.Tensor, scale: float, out: torch.Tensor, lse: torch.Tensor):
+    """``block_fwd`` merged in place into the accumulator (out, lse); returns (out, lse)."""
+    if out is None or lse is None:
+        raise ValueError("block_fwd_merge needs the accumulator tensors out and lse")
+    return _block_fwd_call("cpattn_block_fwd_merge", q, k, v, q_pos, kv_pos, scale, out, lse, alloc=False)
 
 
 def lse_merge(out: torch.Tensor, lse: torch.Tensor, out_tile: torch.Tensor, lse_tile: torch.Tensor):
@@ -194,14 +207,17 @@ def ulysses_heads_to_seq(grouped: torch.Tensor, group: int, out: torch.Tensor) -
 
 def ring_share_fwd(q: torch.Tensor, k_blocks, v_blocks, positions, rank: int, scale: float,
                    out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
-                   tile_out: torch.Tensor | None = None, tile_lse: torch.Tensor | None = None):
+                   tile_out: torch.Tensor | None = None, tile_lse: torch.Tensor | None = None,
+                   fused: bool = True):
     """Rank ``rank``'s share over the C ring steps, back to back on the current stream.
 
     Step i attends the K/V block of owner (rank - i) mod C ("On Context Parallelism",
     Peer-to-peer / Forward): ``k_blocks[o]``, ``v_blocks[o]`` and ``positions[o]`` are owner
     o's shard and its global positions; ``positions[rank]`` are also the query positions.
-    Step 0 writes the accumulator directly; each later step writes a tile and folds it in
-    with ``lse_merge``.  Returns (out, lse).
+    Step 0 writes the accumulator directly.  With ``fused`` each later step merges its block
+    into the accumulator inside the attention launch (``block_fwd_merge``); otherwise it
+    writes a tile (``tile_out``, ``tile_lse``) and folds it in with ``lse_merge``.  Both give
+    the same bits.  Returns (out, lse).
     """
     C = len(k_blocks)
     B, s, Hq, D = q.shape
@@ -209,17 +225,19 @@ def ring_share_fwd(q: torch.Tensor, k_blocks, v_blocks, positions, rank: int, sc
         out = torch.empty((B, s, Hq, D), dtype=torch.float32, device=q.device)
     if lse is None:
         lse = torch.empty((B, Hq, s), dtype=torch.float32, device=q.device)
-    if C > 1:
+    if C > 1 and not fused:
         if tile_out is None:
             tile_out = torch.empty_like(out)
         if tile_lse is None:
             tile_lse = torch.empty_like(lse)
     for step in range(C):
         owner = (rank - step) % C
+        args = (q, k_blocks[owner], v_blocks[owner], positions[rank], positions[owner], scale)
         if step == 0:
-            block_fwd(q, k_blocks[owner], v_blocks[owner], positions[rank], positions[owner], scale, out, lse)
+            block_fwd(*args, out, lse)
+        elif fused:
+            block_fwd_merge(*args, out, lse)
         else:
-            block_fwd(q, k_blocks[owner], v_blocks[owner], positions[rank], positions[owner], scale,
-                      tile_out, tile_lse)
+            block_fwd(*args, tile_out, tile_lse)
             lse_merge(out, lse, tile_out, tile_lse)
     return out, lse

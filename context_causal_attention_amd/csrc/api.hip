@@ -70,48 +70,73 @@ CPATTN_API cpattn_status_t cpattn_zigzag_index(int64_t seq_len, int32_t cp_size,
                     "zigzag_index");
 }
 
+namespace {
+
+// cpattn_block_fwd (merge = false) and cpattn_block_fwd_merge (merge = true) share their
+// validation and dispatch; `name` prefixes the error messages.
+cpattn_status_t block_fwd_common(const char* name, bool merge, const void* q, const void* k,
+                                 const void* v, cpattn_dtype_t dtype, int32_t batch, int64_t seq_q,
+                                 int64_t seq_kv, int32_t heads_q, int32_t heads_kv, int32_t head_dim,
+                                 const int64_t* q_positions, const int64_t* kv_positions, float scale,
+                                 float* out, float* lse, void* stream) {
+    if (dtype != CPATTN_F32 && dtype != CPATTN_BF16)
+        return fail(CPATTN_ERR_INVALID_ARG, "%s: unknown dtype %d", name, (int)dtype);
+    if (batch <= 0 || heads_q <= 0 || heads_kv <= 0)
+        return fail(CPATTN_ERR_INVALID_ARG, "%s: batch and head counts must be > 0", name);
+    if (seq_q < 0 || seq_kv < 0)
+        return fail(CPATTN_ERR_INVALID_ARG, "%s: sequence lengths must be >= 0", name);
+    if (!(scale > 0.f) || !isfinite(scale))
+        return fail(CPATTN_ERR_INVALID_ARG, "%s: scale must be finite and > 0", name);
+    if (heads_q % heads_kv != 0)
+        return fail(CPATTN_ERR_SHAPE, "%s: heads_q %d not a multiple of heads_kv %d", name, heads_q,
+                    heads_kv);
+    if (head_dim != 64 && head_dim != 128)
+        return fail(CPATTN_ERR_UNSUPPORTED, "%s: head_dim %d (supported: 64, 128)", name, head_dim);
+    if (dtype == CPATTN_BF16 && head_dim != 128)
+        return fail(CPATTN_ERR_UNSUPPORTED, "%s: bf16 path supports head_dim 128 only", name);
+    if (seq_q == 0) return ok();
+    if (!q || !q_positions || !out || !lse)
+        return fail(CPATTN_ERR_INVALID_ARG, "%s: q, q_positions, out and lse must be non-NULL", name);
+    if (seq_kv > 0 && (!k || !v || !kv_positions))
+        return fail(CPATTN_ERR_INVALID_ARG, "%s: k, v and kv_positions must be non-NULL", name);
+    if (dtype == CPATTN_BF16 &&
+        (!aligned16(q) || (seq_kv > 0 && (!aligned16(k) || !aligned16(v))) || !aligned16(out)))
+        return fail(CPATTN_ERR_UNSUPPORTED, "%s: bf16 path needs 16-byte aligned q, k, v, out", name);
+    if (dtype == CPATTN_F32 && ((seq_q + 63) / 64 > kMaxGrid || heads_q > 65535 || batch > 65535))
+        return fail(CPATTN_ERR_UNSUPPORTED, "%s: launch grid too large", name);
+    if (dtype == CPATTN_BF16 && (seq_q + 31) / 32 * (int64_t)batch * heads_kv > kMaxGrid)
+        return fail(CPATTN_ERR_UNSUPPORTED, "%s: launch grid too large", name);
+    cpattn::BlockFwdArgs a{q,     k,      v,       q_positions, kv_positions, out,      lse,
+                           batch, seq_q, seq_kv, heads_q,     heads_kv,     head_dim, scale, merge};
+    if (seq_kv == 0) {
+        // no keys at all: every row is empty (out = 0, lse = -inf)
+        return from_hip(cpattn::launch_block_fwd_empty(a, (hipStream_t)stream), name);
+    }
+    const hipError_t e = (dtype == CPATTN_BF16) ? cpattn::launch_block_fwd_bf16(a, (hipStream_t)stream)
+                                                : cpattn::launch_block_fwd_f32(a, (hipStream_t)stream);
+    return from_hip(e, name);
+}
+
+}  // namespace
+
 CPATTN_API cpattn_status_t cpattn_block_fwd(const void* q, const void* k, const void* v,
                                             cpattn_dtype_t dtype, int32_t batch, int64_t seq_q,
                                             int64_t seq_kv, int32_t heads_q, int32_t heads_kv,
                                             int32_t head_dim, const int64_t* q_positions,
                                             const int64_t* kv_positions, float scale, float* out,
                                             float* lse, void* stream) {
-    if (dtype != CPATTN_F32 && dtype != CPATTN_BF16)
-        return fail(CPATTN_ERR_INVALID_ARG, "block_fwd: unknown dtype %d", (int)dtype);
-    if (batch <= 0 || heads_q <= 0 || heads_kv <= 0)
-        return fail(CPATTN_ERR_INVALID_ARG, "block_fwd: batch and head counts must be > 0");
-    if (seq_q < 0 || seq_kv < 0)
-        return fail(CPATTN_ERR_INVALID_ARG, "block_fwd: sequence lengths must be >= 0");
-    if (!(scale > 0.f) || !isfinite(scale))
-        return fail(CPATTN_ERR_INVALID_ARG, "block_fwd: scale must be finite and > 0");
-    if (heads_q % heads_kv != 0)
-        return fail(CPATTN_ERR_SHAPE, "block_fwd: heads_q %d not a multiple of heads_kv %d", heads_q,
-                    heads_kv);
-    if (head_dim != 64 && head_dim != 128)
-        return fail(CPATTN_ERR_UNSUPPORTED, "block_fwd: head_dim %d (supported: 64, 128)", head_dim);
-    if (dtype == CPATTN_BF16 && head_dim != 128)
-        return fail(CPATTN_ERR_UNSUPPORTED, "block_fwd: bf16 path supports head_dim 128 only");
-    if (seq_q == 0) return ok();
-    if (!q || !q_positions || !out || !lse)
-        return fail(CPATTN_ERR_INVALID_ARG, "block_fwd: q, q_positions, out and lse must be non-NULL");
-    if (seq_kv > 0 && (!k || !v || !kv_positions))
-        return fail(CPATTN_ERR_INVALID_ARG, "block_fwd: k, v and kv_positions must be non-NULL");
-    if (dtype == CPATTN_BF16 &&
-        (!aligned16(q) || (seq_kv > 0 && (!aligned16(k) || !aligned16(v))) || !aligned16(out)))
-        return fail(CPATTN_ERR_UNSUPPORTED, "block_fwd: bf16 path needs 16-byte aligned q, k, v, out");
-    if (dtype == CPATTN_F32 && ((seq_q + 63) / 64 > kMaxGrid || heads_q > 65535 || batch > 65535))
-        return fail(CPATTN_ERR_UNSUPPORTED, "block_fwd: launch grid too large");
-    if (dtype == CPATTN_BF16 && (seq_q + 31) / 32 * (int64_t)batch * heads_kv > kMaxGrid)
-        return fail(CPATTN_ERR_UNSUPPORTED, "block_fwd: launch grid too large");
-    cpattn::BlockFwdArgs a{q,     k,      v,       q_positions, kv_positions, out,      lse,
-                           batch, seq_q, seq_kv, heads_q,     heads_kv,     head_dim, scale};
-    if (seq_kv == 0) {
-        // no keys at all: every row is empty (out = 0, lse = -inf)
-        return from_hip(cpattn::launch_block_fwd_empty(a, (hipStream_t)stream), "block_fwd");
-    }
-    const hipError_t e = (dtype == CPATTN_BF16) ? cpattn::launch_block_fwd_bf16(a, (hipStream_t)stream)
-                                                : cpattn::launch_block_fwd_f32(a, (hipStream_t)stream);
-    return from_hip(e, "block_fwd");
+    return block_fwd_common("block_fwd", false, q, k, v, dtype, batch, seq_q, seq_kv, heads_q, heads_kv,
+                            head_dim, q_positions, kv_positions, scale, out, lse, stream);
+}
+
+CPATTN_API cpattn_status_t cpattn_block_fwd_merge(const void* q, const void* k, const void* v,
+                                                  cpattn_dtype_t dtype, int32_t batch, int64_t seq_q,
+                                                  int64_t seq_kv, int32_t heads_q, int32_t heads_kv,
+                                                  int32_t head_dim, const int64_t* q_positions,
+                                                  const int64_t* kv_positions, float scale, float* out,
+                                                  float* lse, void* stream) {
+    return block_fwd_common("block_fwd_merge", true, q, k, v, dtype, batch, seq_q, seq_kv, heads_q,
+                            heads_kv, head_dim, q_positions, kv_positions, scale, out, lse, stream);
 }
 
 CPATTN_API cpattn_status_t cpattn_lse_merge(float* out, float* lse, const float* out_tile,

@@ -37,6 +37,7 @@
 // are a shorter prefix; only the tiles in between are masked element by element.
 // Rows with no visible key end with out = 0 and lse = -inf.
 #include "cpattn_internal.h"
+#include "merge_math.h"
 
 #include <math.h>
 
@@ -80,6 +81,7 @@ struct Params {
     int32_t n_cols;    // batch * heads_kv * n_hg
     int32_t xcd_cols;  // n_cols / 8 when n_cols % 8 == 0, else 0
     float c;           // scale * log2(e)
+    int32_t merge;     // merge into (out, lse) instead of overwriting them
 };
 
 __device__ inline int wave_sum(int x) {
@@ -410,7 +412,7 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
         if (jt + 1 < n_ne) tile(jt + 1, st1, st0);
     }
 
-    // ---- epilogue: combine the half-wave row sums, normalise, store
+    // ---- epilogue: combine the half-wave row sums, normalise, store (or merge into out, lse)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         const float l_tot = half_sum(l_run[nb]);
@@ -418,6 +420,27 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
         const float inv = any ? 1.f / l_tot : 0.f;
         if (myq[nb] >= p.seq_q) continue;
         float* orow = p.out + ((b * p.seq_q + myq[nb]) * p.heads_q + myh[nb]) * kD;
+        float* lrow = p.lse + (b * p.heads_q + myh[nb]) * p.seq_q + myq[nb];
+        const float lse_t = any ? (m_run[nb] + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+        if (p.merge) {
+            // both half-waves read the accumulator's lse before either writes it back
+            const MergeWeights mw = merge_weights(*lrow, lse_t);
+#pragma unroll
+            for (int db = 0; db < kD / 32; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    float4* dst = (float4*)(orow + 32 * db + 8 * g + 4 * half);
+                    const float4 x = *dst;
+                    float4 o4;
+                    o4.x = merge_value(x.x, acc_o[nb][db][4 * g + 0] * inv, mw.w_old, mw.w_new);
+                    o4.y = merge_value(x.y, acc_o[nb][db][4 * g + 1] * inv, mw.w_old, mw.w_new);
+                    o4.z = merge_value(x.z, acc_o[nb][db][4 * g + 2] * inv, mw.w_old, mw.w_new);
+                    o4.w = merge_value(x.w, acc_o[nb][db][4 * g + 3] * inv, mw.w_old, mw.w_new);
+                    *dst = o4;
+                }
+            if (half == 0) *lrow = mw.lse;
+            continue;
+        }
 #pragma unroll
         for (int db = 0; db < kD / 32; ++db)
 #pragma unroll
@@ -429,9 +452,7 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
                 o4.w = acc_o[nb][db][4 * g + 3] * inv;
                 *(float4*)(orow + 32 * db + 8 * g + 4 * half) = o4;
             }
-        if (half == 0)
-            p.lse[(b * p.heads_q + myh[nb]) * p.seq_q + myq[nb]] =
-                any ? (m_run[nb] + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+        if (half == 0) *lrow = lse_t;
     }
 }
 
@@ -465,6 +486,7 @@ hipError_t launch_block_fwd_bf16(const BlockFwdArgs& a, hipStream_t stream) {
     p.n_cols = a.batch * a.heads_kv * p.n_hg;
     p.xcd_cols = (p.n_cols % 8 == 0) ? p.n_cols / 8 : 0;
     p.c = a.scale * kLog2e;
+    p.merge = a.merge ? 1 : 0;
     // 8 waves x 32 rows per block; 4 waves x 32 rows when that would leave the chip less
     // than half full
     const int64_t blocks8 = ((a.seq_q + 256 / p.G - 1) / (256 / p.G)) * p.n_cols;

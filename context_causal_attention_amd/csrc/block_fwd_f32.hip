@@ -9,6 +9,7 @@
 // their positions are staged in LDS and read by broadcast.  Only tiles whose first key is
 // visible to the block's last query are visited.
 #include "cpattn_internal.h"
+#include "merge_math.h"
 
 #include <math.h>
 
@@ -24,7 +25,7 @@ __global__ void __launch_bounds__(kRows) block_fwd_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const int64_t* __restrict__ q_pos, const int64_t* __restrict__ kv_pos, float* __restrict__ out,
     float* __restrict__ lse, int64_t seq_q, int64_t seq_kv, int32_t heads_q, int32_t heads_kv,
-    float scale) {
+    float scale, int merge) {
     __shared__ float ks[kTile][D];
     __shared__ float vs[kTile][D];
     __shared__ int64_t ps[kTile];
@@ -97,9 +98,18 @@ __global__ void __launch_bounds__(kRows) block_fwd_f32_kernel(
     if (!valid) return;
     const float inv = l > 0.f ? 1.f / l : 0.f;
     float* orow = out + ((b * seq_q + i) * heads_q + h) * D;
+    float* lrow = lse + (b * heads_q + h) * seq_q + i;
+    const float lse_t = l > 0.f ? m + logf(l) : -INFINITY;
+    if (merge) {
+        const MergeWeights mw = merge_weights(*lrow, lse_t);
 #pragma unroll
-    for (int d = 0; d < D; ++d) orow[d] = o[d] * inv;
-    lse[(b * heads_q + h) * seq_q + i] = l > 0.f ? m + logf(l) : -INFINITY;
+        for (int d = 0; d < D; ++d) orow[d] = merge_value(orow[d], o[d] * inv, mw.w_old, mw.w_new);
+        *lrow = mw.lse;
+    } else {
+#pragma unroll
+        for (int d = 0; d < D; ++d) orow[d] = o[d] * inv;
+        *lrow = lse_t;
+    }
 }
 
 // A block with no keys at all: every row is empty (out = 0, lse = -inf).
@@ -110,10 +120,33 @@ __global__ void __launch_bounds__(256) empty_rows_kernel(float* __restrict__ out
     for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n_lse; e += stride) lse[e] = -INFINITY;
 }
 
+// Merging an empty result (0, -inf) into an accumulator: one thread per (b, h, i) row.
+// Rows with a finite lse keep their bits; rows at -inf become (0, -inf).
+__global__ void __launch_bounds__(256) merge_empty_kernel(float* __restrict__ out, float* __restrict__ lse,
+                                                          int64_t seq, int32_t heads, int32_t head_dim,
+                                                          int64_t n_rows) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t li = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; li < n_rows; li += stride) {
+        // lse index (b*heads + h)*seq + i  <->  out row (b*seq + i)*heads + h
+        const int64_t i = li % seq, bh = li / seq;
+        const int64_t h = bh % heads, b = bh / heads;
+        const MergeWeights mw = merge_weights(lse[li], -INFINITY);
+        float* orow = out + ((b * seq + i) * heads + h) * head_dim;
+        for (int d = 0; d < head_dim; ++d) orow[d] = merge_value(orow[d], 0.f, mw.w_old, mw.w_new);
+        lse[li] = mw.lse;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_block_fwd_empty(const BlockFwdArgs& a, hipStream_t stream) {
     const int64_t n_lse = (int64_t)a.batch * a.heads_q * a.seq_q;
+    if (a.merge) {
+        const int64_t rb = (n_lse + 255) / 256;
+        hipLaunchKernelGGL(merge_empty_kernel, dim3((unsigned)(rb < 16384 ? rb : 16384)), dim3(256), 0, stream,
+                           a.out, a.lse, a.seq_q, a.heads_q, a.head_dim, n_lse);
+        return hipGetLastError();
+    }
     const int64_t n_out = n_lse * a.head_dim;
     const int64_t blocks = (n_out + 255) / 256;
     hipLaunchKernelGGL(empty_rows_kernel, dim3((unsigned)(blocks < 16384 ? blocks : 16384)), dim3(256), 0,
@@ -128,10 +161,10 @@ hipError_t launch_block_fwd_f32(const BlockFwdArgs& a, hipStream_t stream) {
     const float* v = (const float*)a.v;
     if (a.head_dim == 64)
         hipLaunchKernelGGL(block_fwd_f32_kernel<64>, grid, dim3(kRows), 0, stream, q, k, v, a.q_pos,
-                           a.kv_pos, a.out, a.lse, a.seq_q, a.seq_kv, a.heads_q, a.heads_kv, a.scale);
+                           a.kv_pos, a.out, a.lse, a.seq_q, a.seq_kv, a.heads_q, a.heads_kv, a.scale, (int)a.merge);
     else
         hipLaunchKernelGGL(block_fwd_f32_kernel<128>, grid, dim3(kRows), 0, stream, q, k, v, a.q_pos,
-                           a.kv_pos, a.out, a.lse, a.seq_q, a.seq_kv, a.heads_q, a.heads_kv, a.scale);
+                           a.kv_pos, a.out, a.lse, a.seq_q, a.seq_kv, a.heads_q, a.heads_kv, a.scale, (int)a.merge);
     return hipGetLastError();
 }
 

@@ -38,9 +38,12 @@ struct BlockFwdArgs {
     int32_t heads_kv;
     int32_t head_dim;
     float scale;
+    // false: write the block's (out, lse).  true: (out, lse) hold an accumulator and the
+    // block's result is merged into it in the epilogue, with the arithmetic of merge_math.h.
+    bool merge;
 };
 
-// No keys: writes out = 0 and lse = -inf for every row.
+// No keys: writes out = 0 and lse = -inf for every row (merge: merges that empty result).
 hipError_t launch_block_fwd_empty(const BlockFwdArgs& a, hipStream_t stream);
 // fp32 inputs, fp32 arithmetic on the vector ALUs.
 hipError_t launch_block_fwd_f32(const BlockFwdArgs& a, hipStream_t stream);

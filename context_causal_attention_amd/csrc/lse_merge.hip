@@ -1,12 +1,11 @@
-// In-place merge of a completed partial attention result into an accumulator.
-// "On Context Parallelism", section Peer-to-peer (merging attention tiles): the merged
-// log-sum-exp is ln(e^lse + e^lse_tile) and each side's output is weighted by
-// e^(its lse - merged).  An empty side (lse = -inf) weighs 0; two empty sides give (0, -inf).
+// In-place merge of a completed partial attention result into an accumulator, with the
+// arithmetic of merge_math.h ("On Context Parallelism", section Peer-to-peer).
 //
 // Bandwidth-bound: per row of head_dim floats it reads out and out_tile and writes out.
 // A block owns ROWS consecutive (b, i, h) rows: it first turns their lse pairs into the two
 // weights (in LDS), then streams the rows with 16-byte accesses.
 #include "cpattn_internal.h"
+#include "merge_math.h"
 
 #include <math.h>
 
@@ -15,13 +14,6 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kRows = 64;
-
-// ln(e^a + e^b), symmetric in a and b; -inf when both are -inf.
-__device__ inline float log_add_exp(float a, float b) {
-    const float hi = fmaxf(a, b), lo = fminf(a, b);
-    if (hi == -INFINITY) return -INFINITY;
-    return hi + log1pf(expf(lo - hi));
-}
 
 __global__ void __launch_bounds__(kThreads) lse_merge_kernel(
     float* __restrict__ out, float* __restrict__ lse, const float* __restrict__ out_t,
@@ -37,12 +29,10 @@ __global__ void __launch_bounds__(kThreads) lse_merge_kernel(
         const int64_t bi = row / heads;
         const int64_t i = bi % seq, b = bi / seq;
         const int64_t li = (b * heads + h) * seq + i;
-        const float a = lse[li], c = lse_t[li];
-        const float m = log_add_exp(a, c);
-        const bool empty = (m == -INFINITY);
-        w_old[tid] = empty ? 0.f : expf(a - m);
-        w_new[tid] = empty ? 0.f : expf(c - m);
-        lse[li] = m;
+        const MergeWeights mw = merge_weights(lse[li], lse_t[li]);
+        w_old[tid] = mw.w_old;
+        w_new[tid] = mw.w_new;
+        lse[li] = mw.lse;
     }
     __syncthreads();
     const int vec_per_row = head_dim / 4;
@@ -51,17 +41,14 @@ __global__ void __launch_bounds__(kThreads) lse_merge_kernel(
     float4* o4 = reinterpret_cast<float4*>(out + row0 * head_dim);
     const float4* t4 = reinterpret_cast<const float4*>(out_t + row0 * head_dim);
     for (int e = tid; e < n_vec; e += kThreads) {
-        // two rounded products and a rounded sum (contraction into a fused multiply-add is
-        // off), so the result does not depend on which operand is the accumulator
-#pragma clang fp contract(off)
         const int r = e / vec_per_row;
         const float a = w_old[r], c = w_new[r];
         const float4 x = o4[e], y = t4[e];
         float4 z;
-        z.x = a * x.x + c * y.x;
-        z.y = a * x.y + c * y.y;
-        z.z = a * x.z + c * y.z;
-        z.w = a * x.w + c * y.w;
+        z.x = merge_value(x.x, y.x, a, c);
+        z.y = merge_value(x.y, y.y, a, c);
+        z.z = merge_value(x.z, y.z, a, c);
+        z.w = merge_value(x.w, y.w, a, c);
         o4[e] = z;
     }
 }

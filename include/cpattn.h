@@ -119,6 +119,34 @@ cpattn_status_t cpattn_block_fwd(const void* q, const void* k, const void* v, cp
                                  void* stream);
 
 /*
+ * cpattn_block_fwd_merge -- cpattn_block_fwd with its result folded into an accumulator
+ * in the same launch.  A ring step of [CP] "Peer-to-peer" / "Forward" computes one block's
+ * (out_tile, lse_tile) and merges it into the running result (the merge discussion of the
+ * same section); here the kernel's epilogue does the merge, so the tile never reaches
+ * memory.  With (o, l) the values cpattn_block_fwd would write for the same arguments:
+ *
+ *   merged = ln(exp(lse) + exp(l))
+ *   out    = exp(lse - merged) * out + exp(l - merged) * o
+ *   lse    = merged
+ *
+ * with the rounding of cpattn_lse_merge: the result has the same bits as cpattn_block_fwd
+ * into a scratch tile followed by cpattn_lse_merge into (out, lse).
+ *
+ *   q, k, v, positions, scale, dtype   as for cpattn_block_fwd
+ *   out   in/out fp32 [batch][seq_q][heads_q][head_dim], the accumulator
+ *   lse   in/out fp32 [batch][heads_q][seq_q], the accumulator (-inf marks "nothing yet";
+ *         out must then hold finite values, e.g. 0)
+ * seq_q == 0 is a no-op; seq_kv == 0 merges an empty result (rows at -inf become out = 0).
+ * Errors as for cpattn_block_fwd.
+ */
+cpattn_status_t cpattn_block_fwd_merge(const void* q, const void* k, const void* v,
+                                       cpattn_dtype_t dtype, int32_t batch, int64_t seq_q,
+                                       int64_t seq_kv, int32_t heads_q, int32_t heads_kv,
+                                       int32_t head_dim, const int64_t* q_positions,
+                                       const int64_t* kv_positions, float scale, float* out,
+                                       float* lse, void* stream);
+
+/*
  * cpattn_lse_merge -- fold one completed partial result into an accumulator, in place.
  * [CP] "Peer-to-peer" (merging attention tiles) and [HB] "Ring Attention":
  *

@@ -46,7 +46,8 @@ def max_abs(a, b) -> float:
     a = np.asarray(a, dtype=np.float64)
     b = np.asarray(b, dtype=np.float64)
     both_inf = np.isinf(a) & np.isinf(b) & (np.sign(a) == np.sign(b))
-    d = np.where(both_inf, 0.0, np.abs(a - b))
+    with np.errstate(invalid="ignore"):  # inf - inf on the rows excluded by both_inf
+        d = np.where(both_inf, 0.0, np.abs(a - b))
     return float(np.nan_to_num(d, nan=np.inf).max()) if d.size else 0.0
 
 

@@ -117,3 +117,22 @@ def test_binding_refuses_cpu_tensors():
     pos = torch.arange(8)
     with pytest.raises(ValueError, match="GPU tensor"):
         cp.block_fwd(x, x, x, pos, pos, 0.1)
+
+
+def test_block_fwd_merge_validation(lib):
+    """The merging entry point validates exactly like cpattn_block_fwd."""
+    def bfm(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=1, batch=1, seq_q=64, seq_kv=64, hq=4, hkv=2, d=128,
+                 qpos=FAKE, kvpos=FAKE, scale=0.1, out=FAKE, lse=FAKE)
+        a.update(kw)
+        return lib.cpattn_block_fwd_merge(a["q"], a["k"], a["v"], a["dtype"], a["batch"], a["seq_q"],
+                                          a["seq_kv"], a["hq"], a["hkv"], a["d"], a["qpos"], a["kvpos"],
+                                          a["scale"], a["out"], a["lse"], NULL)
+    assert bfm(dtype=7) == INVALID and _err(lib).startswith("block_fwd_merge:")
+    assert bfm(batch=0) == INVALID
+    assert bfm(scale=float("nan")) == INVALID
+    assert bfm(hq=6, hkv=4) == SHAPE
+    assert bfm(d=64, dtype=1) == UNSUPPORTED
+    assert bfm(lse=NULL) == INVALID
+    assert bfm(out=ctypes.c_void_p(0x1004)) == UNSUPPORTED
+    assert bfm(seq_q=0, q=NULL, out=NULL, lse=NULL, qpos=NULL) == OK
