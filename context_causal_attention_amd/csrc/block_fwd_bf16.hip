@@ -18,12 +18,14 @@
 //                  B = 16 dims x 32 queries of Q (registers, loaded once).  The accumulator
 //                  gives each lane 16 keys of ONE query, so the row max is lane-local plus
 //                  one exchange with the other half-wave.
-//   softmax in the log2 domain (scores times scale*log2(e), exp2).  The running max is only
-//                  raised when a row's tile max exceeds it by more than kLazy (2^8 in weight):
-//                  the result is the same for any reference value, and skipping the raise
-//                  skips rescaling the accumulator.  Weights stay <= 2^8.
-//   P rounded to bf16 (RNE) straight from the accumulator registers; the row sum adds the
-//                  fp32 weights (rounding them first would cost lse up to 2^-9 on short rows).
+//   softmax in the log2 domain (scores times scale*log2(e), exp2) against a running
+//                  reference m that is not necessarily the row max: the result is the same
+//                  for any reference.  Each tile first takes the weights against the current
+//                  m.  Only when some lane's sum of them exceeds 2^kLazy (or m is still unset)
+//                  does the wave compute the row max, raise m to it, rescale the accumulator
+//                  and recompute; so weights stay <= 2^kLazy and most tiles need no max.
+//   P rounded to bf16 (RNE) straight from the weights; the row sum adds the fp32 weights
+//                  (rounding them first would cost lse up to 2^-9 on short rows).
 //   O^T += V^T P^T with A = 32 dims x 16 keys of V read transposed from the row-major LDS
 //                  tile by ds_read_b64_tr_b16, B = P^T (registers).  The key order inside a
 //                  16-key step is the accumulator's own order, applied to V's addresses.
@@ -34,7 +36,8 @@
 // Causal skip ("Context parallelism: Ring Attention and Ulysses", Ring Attention: blocks
 // later than the query are skipped whole): with strictly increasing positions the visible
 // tiles of a block are a prefix, and the tiles entirely visible to every query of the block
-// are a shorter prefix; only the tiles in between are masked element by element.
+// are a shorter prefix; only the tiles in between are masked element by element, against
+// each row's count of visible keys (found once by binary search over the key positions).
 // Rows with no visible key end with out = 0 and lse = -inf.
 #include "cpattn_internal.h"
 #include "merge_math.h"
@@ -60,6 +63,7 @@ constexpr int kTileBytes = kBN * kRowBytes;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.0f;       // raise the running max only past this margin (log2)
+constexpr float kLazyWeight = 256.0f;  // 2^kLazy
 
 struct Params {
     const __bf16* q;
@@ -108,13 +112,6 @@ __device__ inline bf16x8 lds_tr_pair(const LDS_AS char* p0, const LDS_AS char* p
     const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)p1);
     const s16x8 c = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
     return __builtin_bit_cast(bf16x8, c);
-}
-
-__device__ inline bf16x8 pack_bf16(const f32x16& s, int base) {
-    bf16x8 r;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) r[j] = (__bf16)s[base + j];
-    return r;
 }
 
 // One 16-byte direct global->LDS load: this lane's 16 bytes land at lds_base + 16*lane.
@@ -256,6 +253,25 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
         }
     }
 
+    // number of keys visible to each of this lane's query rows, needed only when some tile
+    // is partly visible: positions increase, so it is found by binary search within the
+    // keys of the partly visible tiles [n_full*kBN, min(n_ne*kBN, seq_kv))
+    int64_t vis[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) vis[nb] = 0;
+    if (n_full < n_ne) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            int64_t lo = (int64_t)n_full * kBN;
+            int64_t hi = (int64_t)n_ne * kBN < p.seq_kv ? (int64_t)n_ne * kBN : p.seq_kv;
+            while (lo < hi) {
+                const int64_t mid = (lo + hi) >> 1;
+                if (p.kvpos[mid] <= mypos[nb]) lo = mid + 1; else hi = mid;
+            }
+            vis[nb] = lo;
+        }
+    }
+
     f32x16 acc_o[NB][kD / 32];
     float m_run[NB], l_run[NB];
 #pragma unroll
@@ -319,61 +335,67 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
         __builtin_amdgcn_sched_group_barrier(0x008, NB * kReadAheadK, 1);
 
         // element mask on tiles not entirely visible: key index of accumulator entry v is
-        // 32*kb + 8*(v/4) + 4*half + v%4
+        // 32*kb + 8*(v/4) + 4*half + v%4 within the tile; visible iff below the row's count
         if (jt >= n_full) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+            for (int nb = 0; nb < NB; ++nb) {
+                const int64_t rel = vis[nb] - (int64_t)jt * kBN - 4 * half;
+                const int lim = rel < 0 ? 0 : (rel > kBN ? kBN : (int)rel);
 #pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
-                    const int64_t j0 = (int64_t)jt * kBN + 32 * kb + 8 * g4 + 4 * half;
+                for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int64_t j = j0 + e;
-                        const int64_t kp = (j < p.seq_kv) ? p.kvpos[j] : INT64_MAX;
-#pragma unroll
-                        for (int nb = 0; nb < NB; ++nb)
-                            if (kp > mypos[nb]) s[nb][kb][4 * g4 + e] = -INFINITY;
-                    }
-                }
+                    for (int v = 0; v < 16; ++v)
+                        if (32 * kb + 8 * (v / 4) + v % 4 >= lim) s[nb][kb][v] = -INFINITY;
             }
         }
 
-        // softmax, log2 domain, lazy raise of the running max
+        // softmax in the log2 domain against the running reference m.  Fast path: weights
+        // against the current m; they stay bounded (each at most 2^kLazy) whenever this lane's
+        // sum of them does, so no row max is needed.  Otherwise (or while m is unset) the
+        // wave takes the slow path: row max, raise m to it, rescale O and l, recompute.
         bf16x8 pb[NB][2][2];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            float mx = -INFINITY;
+            float m_use = (m_run[nb] == -INFINITY) ? 0.f : m_run[nb];
+            float ts = 0.f;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int vv = 0; vv < 16; ++vv) mx = fmaxf(mx, s[nb][kb][vv]);
-            const float mt = half_max(mx) * p.c;
-            // raise only when some row of the wave gained more than kLazy (wave-uniform)
-            if (__builtin_amdgcn_ballot_w64(mt > m_run[nb] + kLazy) != 0) {
+                for (int h8 = 0; h8 < 2; ++h8)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const float e = __builtin_amdgcn_exp2f(fmaf(s[nb][kb][8 * h8 + j], p.c, -m_use));
+                        ts += e;
+                        pb[nb][kb][h8][j] = (__bf16)e;
+                    }
+            const bool bad = !(ts <= kLazyWeight) || m_run[nb] == -INFINITY;
+            if (__builtin_amdgcn_ballot_w64(bad) != 0) {
+                float mx = -INFINITY;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int vv = 0; vv < 16; ++vv) mx = fmaxf(mx, s[nb][kb][vv]);
+                const float mt = half_max(mx) * p.c;
                 const float m_new = fmaxf(m_run[nb], mt);
-                const float m_new_use = (m_new == -INFINITY) ? 0.f : m_new;
-                const float alpha = __builtin_amdgcn_exp2f(m_run[nb] - m_new_use);
+                m_use = (m_new == -INFINITY) ? 0.f : m_new;
+                const float alpha = __builtin_amdgcn_exp2f(m_run[nb] - m_use);
                 l_run[nb] *= alpha;
 #pragma unroll
                 for (int db = 0; db < kD / 32; ++db) acc_o[nb][db] *= alpha;
                 m_run[nb] = m_new;
+                ts = 0.f;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int h8 = 0; h8 < 2; ++h8)
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            const float e = __builtin_amdgcn_exp2f(fmaf(s[nb][kb][8 * h8 + j], p.c, -m_use));
+                            ts += e;
+                            pb[nb][kb][h8][j] = (__bf16)e;
+                        }
             }
-            const float m_use = (m_run[nb] == -INFINITY) ? 0.f : m_run[nb];
-            float rs = l_run[nb];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int vv = 0; vv < 16; ++vv) {
-                    const float e = __builtin_amdgcn_exp2f(fmaf(s[nb][kb][vv], p.c, -m_use));
-                    s[nb][kb][vv] = e;
-                    rs += e;
-                }
-            l_run[nb] = rs;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                pb[nb][kb][0] = pack_bf16(s[nb][kb], 0);
-                pb[nb][kb][1] = pack_bf16(s[nb][kb], 8);
-            }
+            l_run[nb] += ts;
         }
 
         // O^T += V^T P^T
