@@ -14,6 +14,9 @@ the pages step by step:
 * ``closed_form_share``: the same blocks folded at once with the boxed combine of
   "Context parallelism -- splitting the sequence across GPUs", section "How do partial
   softmax results combine?".
+* the zigzag Ulysses exchange (the all-to-all's rank-order concatenation followed by the
+  chunk reorder) and the two-dimensional mesh of "On Context Parallelism", section
+  "Peer-to-peer + All-to-all" (group positions, rank coordinates, the group's share).
 * the work models of "Context Parallelism & Ring Attention" ("The causal load-imbalance
   problem", "The zigzag fix") and of "Context parallelism: Ring Attention and Ulysses"
   ("The zigzag partition", "Ring Attention").
@@ -142,6 +145,21 @@ def ulysses_heads_to_seq(grouped: np.ndarray, C: int, g: int, out: np.ndarray) -
     return out
 
 
+def ulysses_zigzag_seq_to_heads(stacked: np.ndarray, C: int, g: int) -> np.ndarray:
+    """Zigzag shards [C, B, S/C, H, D] through the Ulysses exchange for head group g.
+
+    "On Context Parallelism", section "All-to-all": the exchange concatenates the C shards
+    in rank order; with zigzag shards that is the rank-order layout of section "All-gather"
+    ([c0, c2C-1, c1, c2C-2, ...]), which the chunk reorder turns into global order."""
+    return reorder(ulysses_seq_to_heads(stacked, C, g), C, 0)
+
+
+def ulysses_zigzag_heads_to_seq(grouped: np.ndarray, C: int, g: int, out: np.ndarray) -> np.ndarray:
+    """Inverse of ``ulysses_zigzag_seq_to_heads``: global order back to rank order, then the
+    exchange back to group g's heads of the stacked shards ``out``."""
+    return ulysses_heads_to_seq(reorder(grouped, C, 1), C, g, out)
+
+
 # ----------------------------------------------------------------------------------------
 # Attention
 # ----------------------------------------------------------------------------------------
@@ -267,6 +285,49 @@ def closed_form_share(q_local, k_full, v_full, S: int, C: int, r: int, scale: fl
             out[b, :, h] = o
             lse[b, h] = L
     return out, lse
+
+
+# ----------------------------------------------------------------------------------------
+# Two-dimensional mesh ("On Context Parallelism", "Peer-to-peer + All-to-all")
+# ----------------------------------------------------------------------------------------
+def usp_rank_coords(r: int, A: int) -> tuple[int, int]:
+    """Rank r of C = A*R: A2A groups are runs of A consecutive ranks ([0,1], [2,3], ... at
+    A=2) and P2P groups collect the ranks at the same place in their A2A group ([0,2,4,6]
+    and [1,3,5,7] at C=8, A=2).  Returns (A2A group = position in the P2P ring, place in
+    the A2A group = head group)."""
+    return r // A, r % A
+
+
+def usp_groups(C: int, A: int) -> tuple[list[list[int]], list[list[int]]]:
+    """(A2A groups, P2P groups) of C ranks, each group's ranks in increasing order."""
+    a2a, p2p = {}, {}
+    for r in range(C):
+        g, a = usp_rank_coords(r, A)
+        a2a.setdefault(g, []).append(r)
+        p2p.setdefault(a, []).append(r)
+    return [a2a[k] for k in sorted(a2a)], [p2p[k] for k in sorted(p2p)]
+
+
+def group_positions(S: int, A: int, R: int, g: int) -> np.ndarray:
+    """Global positions held by A2A group g after its exchange: the union of its A ranks'
+    zigzag shards over C = A*R ranks, in increasing order."""
+    C = A * R
+    return np.sort(np.concatenate([zigzag_positions(S, C, g * A + j) for j in range(A)]))
+
+
+def usp_rank_share(q_full, k_full, v_full, S: int, A: int, R: int, r: int, scale: float,
+                   rows=None, nthreads: int | None = None):
+    """Rank r's share on the mesh, by the definition: its A2A group's tokens (in increasing
+    position order) and its head group (Hq/A query heads, Hkv/A kv heads) attend the whole
+    sequence causally.  q_full [B, S, Hq, D], k_full and v_full [B, S, Hkv, D] in global
+    order.  Returns (out [B, S/R, Hq/A, D], lse [B, Hq/A, S/R])."""
+    g, a = usp_rank_coords(r, A)
+    pos = group_positions(S, A, R, g)
+    hq, hk = np.asarray(q_full).shape[2] // A, np.asarray(k_full).shape[2] // A
+    q = np.asarray(q_full)[:, pos][:, :, a * hq:(a + 1) * hq]
+    k = np.asarray(k_full)[:, :, a * hk:(a + 1) * hk]
+    v = np.asarray(v_full)[:, :, a * hk:(a + 1) * hk]
+    return attention_rows(q, k, v, pos, np.arange(S, dtype=np.int64), scale, rows, nthreads)
 
 
 # ----------------------------------------------------------------------------------------
