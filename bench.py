@@ -105,11 +105,19 @@ class Plan:
             self.reorder_bytes = 2 * 2 * self.kg.numel() * self.kg.element_size()
         elif w.kind == "ulysses":
             s, g = w.local_len, w.group
-            stack = lambda x: x.reshape(w.batch, C, s, *x.shape[2:]).transpose(0, 1).contiguous()
-            ids = range(2 * C)
-            self.qst = stack(synthetic.chunks("q", ids, heads=w.heads_q, **kw)).to(dev)
-            self.kst = stack(synthetic.chunks("k", ids, heads=w.heads_kv, **kw)).to(dev)
-            self.vst = stack(synthetic.chunks("v", ids, heads=w.heads_kv, **kw)).to(dev)
+            if w.zigzag:
+                # rank src's shard: chunks src and 2C-1-src
+                shard = lambda name, H, src: synthetic.chunks(name, [src, 2 * C - 1 - src], heads=H, **kw)
+                stack_z = lambda name, H: torch.stack([shard(name, H, src) for src in range(C)]).to(dev)
+                self.qst = stack_z("q", w.heads_q)
+                self.kst = stack_z("k", w.heads_kv)
+                self.vst = stack_z("v", w.heads_kv)
+            else:
+                stack = lambda x: x.reshape(w.batch, C, s, *x.shape[2:]).transpose(0, 1).contiguous()
+                ids = range(2 * C)
+                self.qst = stack(synthetic.chunks("q", ids, heads=w.heads_q, **kw)).to(dev)
+                self.kst = stack(synthetic.chunks("k", ids, heads=w.heads_kv, **kw)).to(dev)
+                self.vst = stack(synthetic.chunks("v", ids, heads=w.heads_kv, **kw)).to(dev)
             hq, hk = w.heads_q // C, w.heads_kv // C
             self.qg = torch.empty((w.batch, w.seq_len, hq, w.head_dim), dtype=td, device=dev)
             self.kgp = torch.empty((w.batch, w.seq_len, hk, w.head_dim), dtype=td, device=dev)
@@ -122,6 +130,31 @@ class Plan:
             self.attn_flops.append(4.0 * w.batch * hq * w.head_dim * (S * (S + 1) // 2))
             el = self.qst.element_size()
             self.permute_bytes = 2 * (self.qg.numel() + 2 * self.kgp.numel()) * el + 2 * self.og.numel() * 4
+        elif w.kind == "usp":
+            A = w.a2a
+            R = C // A
+            self.R, self.g, self.a = R, w.rank // A, w.rank % A
+            shard = lambda name, H, r: synthetic.chunks(name, [r, 2 * C - 1 - r], heads=H, **kw)
+            # A2A group o's stacked shards (its A ranks o*A .. o*A+A-1)
+            grp = lambda name, H, o: torch.stack([shard(name, H, o * A + j) for j in range(A)]).to(dev)
+            self.qst = grp("q", w.heads_q, self.g)
+            self.ksts = [grp("k", w.heads_kv, o) for o in range(R)]
+            self.vsts = [grp("v", w.heads_kv, o) for o in range(R)]
+            n = w.seq_len // R
+            hq, hk = w.heads_q // A, w.heads_kv // A
+            self.qh = torch.empty((w.batch, n, hq, w.head_dim), dtype=td, device=dev)
+            self.kh = [torch.empty((w.batch, n, hk, w.head_dim), dtype=td, device=dev) for _ in range(R)]
+            self.vh = [torch.empty((w.batch, n, hk, w.head_dim), dtype=td, device=dev) for _ in range(R)]
+            self.pos = [torch.empty(n, dtype=torch.int64, device=dev) for _ in range(R)]
+            self.out = torch.empty((w.batch, n, hq, w.head_dim), dtype=torch.float32, device=dev)
+            self.lse = torch.empty((w.batch, hq, n), dtype=torch.float32, device=dev)
+            self.ost = torch.zeros((A, w.batch, w.local_len, w.heads_q, w.head_dim), dtype=torch.float32,
+                                   device=dev)
+            t2 = w.seq_len // (2 * R)
+            for step in range(R):
+                owner = (self.g - step) % R
+                pairs = 2 * t2 * t2 + t2 if owner == self.g else 2 * t2 * t2
+                self.attn_flops.append(4.0 * w.batch * hq * w.head_dim * pairs)
         else:
             raise ValueError(w.kind)
         self.flops = sum(self.attn_flops)
@@ -163,13 +196,31 @@ class Plan:
             for rr in range(C):
                 cp.zigzag_index(w.seq_len, C, rr, out=self.pos[rr])
                 attn(self.qs[rr], self.kseq, self.vseq, self.pos[rr], self.gpos, w.scale, self.out, self.lse)
-        else:
-            g = w.group
-            cp.ulysses_seq_to_heads(self.qst, g, out=self.qg)
-            cp.ulysses_seq_to_heads(self.kst, g, out=self.kgp)
-            cp.ulysses_seq_to_heads(self.vst, g, out=self.vgp)
+        elif self.kind == "ulysses":
+            g, zz = w.group, w.zigzag
+            cp.ulysses_seq_to_heads(self.qst, g, out=self.qg, zigzag=zz)
+            cp.ulysses_seq_to_heads(self.kst, g, out=self.kgp, zigzag=zz)
+            cp.ulysses_seq_to_heads(self.vst, g, out=self.vgp, zigzag=zz)
             attn(self.qg, self.kgp, self.vgp, self.gpos, self.gpos, w.scale, self.og, self.lg)
-            cp.ulysses_heads_to_seq(self.og, g, self.ost)
+            cp.ulysses_heads_to_seq(self.og, g, self.ost, zigzag=zz)
+        else:
+            # the group's exchange for this rank's head group (every ring owner's K/V
+            # exchange included, although on a mesh each group does its own), then the
+            # ring over the R owners and the inverse exchange of the output
+            R, g, a = self.R, self.g, self.a
+            cp.ulysses_seq_to_heads(self.qst, a, out=self.qh, zigzag=True)
+            for o in range(R):
+                cp.ulysses_seq_to_heads(self.ksts[o], a, out=self.kh[o], zigzag=True)
+                cp.ulysses_seq_to_heads(self.vsts[o], a, out=self.vh[o], zigzag=True)
+                cp.zigzag_index(w.seq_len, R, o, out=self.pos[o])
+            for step in range(R):
+                owner = (g - step) % R
+                a_ = (self.qh, self.kh[owner], self.vh[owner], self.pos[g], self.pos[owner], w.scale)
+                if step == 0:
+                    attn(*a_, self.out, self.lse)
+                else:
+                    attn(*a_, self.out, self.lse, fn=cp.block_fwd_merge)
+            cp.ulysses_heads_to_seq(self.out, a, self.ost, zigzag=True)
 
 
 def profiled_traffic(workload: str, kernel: str):
@@ -209,6 +260,19 @@ def cpu_baseline(w, budget_s: float):
         k = synthetic.chunks("k", ids, heads=w.heads_kv, **kw)[:, :, g * hk:(g + 1) * hk].float().numpy()
         v = synthetic.chunks("v", ids, heads=w.heads_kv, **kw)[:, :, g * hk:(g + 1) * hk].float().numpy()
         qpos = np.arange(S, dtype=np.int64)
+        heads = hq
+    elif w.kind == "usp":
+        A = w.a2a
+        R = C // A
+        g, a = w.rank // A, w.rank % A
+        hq, hk = w.heads_q // A, w.heads_kv // A
+        ids = list(range(2 * C))
+        qpos = np.sort(np.concatenate([np.arange(c * w.chunk_len, (c + 1) * w.chunk_len)
+                                       for j in range(A) for c in (g * A + j, 2 * C - 1 - g * A - j)]))
+        q = synthetic.chunks("q", ids, heads=w.heads_q, **kw)[:, qpos, a * hq:(a + 1) * hq].float().numpy()
+        k = synthetic.chunks("k", ids, heads=w.heads_kv, **kw)[:, :, a * hk:(a + 1) * hk].float().numpy()
+        v = synthetic.chunks("v", ids, heads=w.heads_kv, **kw)[:, :, a * hk:(a + 1) * hk].float().numpy()
+        qpos = qpos.astype(np.int64)
         heads = hq
     else:
         r = w.rank if w.rank is not None else C - 1  # one rank stands for all: equal work per rank
@@ -293,7 +357,7 @@ def main(argv=None) -> int:
         "dtype": w.dtype,
         "data": "synthetic (seeded iid N(0,1), per-chunk generators)",
         "config": {"workload": w.name + ("_unfused" if args.unfused and w.kind == "ring_share" else ""),
-                   "batch": w.batch, "seq_len": w.seq_len, "cp_size": w.cp_size,
+                   "batch": w.batch, "a2a": w.a2a, "zigzag": w.zigzag, "seq_len": w.seq_len, "cp_size": w.cp_size,
                    "rank": w.rank, "group": w.group, "heads_q": w.heads_q, "heads_kv": w.heads_kv,
                    "head_dim": w.head_dim, "unmasked_flops_per_step": plan.flops},
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),

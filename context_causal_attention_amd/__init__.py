@@ -21,5 +21,7 @@ from ._binding import (  # noqa: F401
     ring_share_fwd,
     ulysses_heads_to_seq,
     ulysses_seq_to_heads,
+    ulysses_share_fwd,
+    usp_share_fwd,
     zigzag_index,
 )

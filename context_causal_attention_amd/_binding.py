@@ -57,8 +57,9 @@ def load_library():
     L.cpattn_lse_merge.argtypes = [P, P, P, P, i32, i64, i32, i32, P]
     L.cpattn_reorder_gathered.argtypes = [P, P, i32, i64, i64, i32, ctypes.c_int, P]
     L.cpattn_ulysses_permute.argtypes = [P, P, i32, i32, i64, i32, i32, i32, i32, ctypes.c_int, P]
+    L.cpattn_ulysses_permute_zigzag.argtypes = list(L.cpattn_ulysses_permute.argtypes)
     for name in ("cpattn_zigzag_index", "cpattn_block_fwd", "cpattn_block_fwd_merge", "cpattn_lse_merge",
-                 "cpattn_reorder_gathered", "cpattn_ulysses_permute"):
+                 "cpattn_reorder_gathered", "cpattn_ulysses_permute", "cpattn_ulysses_permute_zigzag"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -179,29 +180,37 @@ def reorder_gathered(x: torch.Tensor, cp_size: int, direction: int = RANK_TO_SEQ
     return out
 
 
-def ulysses_seq_to_heads(stacked: torch.Tensor, group: int, out: torch.Tensor | None = None) -> torch.Tensor:
-    """Stacked rank shards [C, B, S/C, H, D] -> head group ``group``'s [B, S, H/C, D]."""
+def ulysses_seq_to_heads(stacked: torch.Tensor, group: int, out: torch.Tensor | None = None,
+                         zigzag: bool = False) -> torch.Tensor:
+    """Stacked rank shards [C, B, S/C, H, D] -> head group ``group``'s [B, S, H/C, D].
+
+    ``zigzag``: the shards are zigzag (rank src holds chunks src and 2C-1-src) and the
+    result is in global sequence order; otherwise shards are contiguous."""
     L = load_library()
     _need(stacked, "stacked")
     C, B, s, H, D = stacked.shape
     if out is None:
         out = torch.empty((B, s * C, H // C, D), dtype=stacked.dtype, device=stacked.device)
     _need(out, "out", stacked.dtype, (B, s * C, H // C, D))
-    _check(L.cpattn_ulysses_permute(_ptr(stacked), _ptr(out), stacked.element_size(), B, s * C, H, D,
-                                    C, group, SEQ_TO_HEADS, _stream(stacked.device)))
+    fn = L.cpattn_ulysses_permute_zigzag if zigzag else L.cpattn_ulysses_permute
+    _check(fn(_ptr(stacked), _ptr(out), stacked.element_size(), B, s * C, H, D, C, group, SEQ_TO_HEADS,
+              _stream(stacked.device)))
     return out
 
 
-def ulysses_heads_to_seq(grouped: torch.Tensor, group: int, out: torch.Tensor) -> torch.Tensor:
-    """Head group ``group``'s [B, S, H/C, D] -> its heads of stacked out [C, B, S/C, H, D]."""
+def ulysses_heads_to_seq(grouped: torch.Tensor, group: int, out: torch.Tensor,
+                         zigzag: bool = False) -> torch.Tensor:
+    """Head group ``group``'s [B, S, H/C, D] -> its heads of stacked out [C, B, S/C, H, D]
+    (``zigzag`` as in ``ulysses_seq_to_heads``)."""
     L = load_library()
     _need(grouped, "grouped")
     _need(out, "out", grouped.dtype)
     C, B, s, H, D = out.shape
     if tuple(grouped.shape) != (B, s * C, H // C, D):
         raise ValueError(f"grouped must have shape {(B, s * C, H // C, D)}")
-    _check(L.cpattn_ulysses_permute(_ptr(grouped), _ptr(out), grouped.element_size(), B, s * C, H, D,
-                                    C, group, HEADS_TO_SEQ, _stream(grouped.device)))
+    fn = L.cpattn_ulysses_permute_zigzag if zigzag else L.cpattn_ulysses_permute
+    _check(fn(_ptr(grouped), _ptr(out), grouped.element_size(), B, s * C, H, D, C, group, HEADS_TO_SEQ,
+              _stream(grouped.device)))
     return out
 
 
@@ -240,4 +249,48 @@ def ring_share_fwd(q: torch.Tensor, k_blocks, v_blocks, positions, rank: int, sc
         else:
             block_fwd(*args, tile_out, tile_lse)
             lse_merge(out, lse, tile_out, tile_lse)
+    return out, lse
+
+
+def ulysses_share_fwd(q_st: torch.Tensor, k_st: torch.Tensor, v_st: torch.Tensor, group: int,
+                      scale: float, out_st: torch.Tensor, zigzag: bool = True):
+    """Head group ``group``'s share of Ulysses attention from the stacked rank shards
+    [C, B, S/C, H, D] of Q, K and V ("On Context Parallelism", All-to-all): the
+    sequence-to-heads exchange (zigzag shards: with the chunk reorder folded in), causal
+    attention over the whole sequence on global positions, and the inverse exchange of the
+    output into the group's heads of ``out_st`` (fp32 [C, B, S/C, Hq, D]).
+    Returns (out_grouped [B, S, Hq/C, D], lse [B, Hq/C, S])."""
+    C, B, s, _, _ = q_st.shape
+    S = s * C
+    qg = ulysses_seq_to_heads(q_st, group, zigzag=zigzag)
+    kg = ulysses_seq_to_heads(k_st, group, zigzag=zigzag)
+    vg = ulysses_seq_to_heads(v_st, group, zigzag=zigzag)
+    pos = zigzag_index(S, 1, 0, device=q_st.device)  # 0 .. S-1: global order
+    og, lse = block_fwd(qg, kg, vg, pos, pos, scale)
+    ulysses_heads_to_seq(og, group, out_st, zigzag=zigzag)
+    return og, lse
+
+
+def usp_share_fwd(q_st: torch.Tensor, k_sts, v_sts, ring_rank: int, head_group: int, scale: float,
+                  out_st: torch.Tensor):
+    """One rank's share of the two-dimensional mesh ("On Context Parallelism", Peer-to-peer
+    + All-to-all): C = A*R ranks, A2A groups of A consecutive ranks, P2P rings of the R ranks
+    that hold the same head group.
+
+    ``q_st`` is this rank's A2A group's stacked zigzag shards [A, B, S/C, Hq, D];
+    ``k_sts[o]`` and ``v_sts[o]`` are A2A group o's stacked shards of K and V, for every
+    group o of the ring.  The group's exchange (zigzag, head group ``head_group``) gives
+    [B, S/R, H/A, D] in increasing position order, which are exactly the positions of rank
+    ``ring_rank`` of a zigzag partition of S over R; the ring share then runs over the R
+    owners, and the inverse exchange writes the output into ``out_st`` (fp32
+    [A, B, S/C, Hq, D]).  Returns (out [B, S/R, Hq/A, D], lse [B, Hq/A, S/R])."""
+    A, B, s, _, _ = q_st.shape
+    R = len(k_sts)
+    S = s * A * R
+    qh = ulysses_seq_to_heads(q_st, head_group, zigzag=True)
+    kh = [ulysses_seq_to_heads(k, head_group, zigzag=True) for k in k_sts]
+    vh = [ulysses_seq_to_heads(v, head_group, zigzag=True) for v in v_sts]
+    pos = [zigzag_index(S, R, o, device=q_st.device) for o in range(R)]
+    out, lse = ring_share_fwd(qh, kh, vh, pos, ring_rank, scale)
+    ulysses_heads_to_seq(out, head_group, out_st, zigzag=True)
     return out, lse

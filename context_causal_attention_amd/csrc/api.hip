@@ -184,30 +184,49 @@ CPATTN_API cpattn_status_t cpattn_reorder_gathered(const void* in, void* out, in
                     "reorder_gathered");
 }
 
+namespace {
+
+cpattn_status_t ulysses_common(const char* name, bool zigzag, const void* in, void* out, int32_t elem_bytes,
+                               int32_t batch, int64_t seq_len, int32_t heads, int32_t head_dim,
+                               int32_t cp_size, int32_t group, cpattn_permute_dir_t dir, void* stream) {
+    if (elem_bytes <= 0 || batch <= 0 || seq_len <= 0 || heads <= 0 || head_dim <= 0 || cp_size <= 0)
+        return fail(CPATTN_ERR_INVALID_ARG, "%s: sizes must be > 0", name);
+    if (dir != CPATTN_SEQ_TO_HEADS && dir != CPATTN_HEADS_TO_SEQ)
+        return fail(CPATTN_ERR_INVALID_ARG, "%s: unknown direction %d", name, (int)dir);
+    if (group < 0 || group >= cp_size)
+        return fail(CPATTN_ERR_INVALID_ARG, "%s: group %d outside [0, %d)", name, group, cp_size);
+    if (!in || !out) return fail(CPATTN_ERR_INVALID_ARG, "%s: NULL pointer", name);
+    if (in == out) return fail(CPATTN_ERR_INVALID_ARG, "%s: in and out must differ", name);
+    const int64_t div = zigzag ? 2 * (int64_t)cp_size : cp_size;
+    if (seq_len % div != 0)
+        return fail(CPATTN_ERR_SHAPE, "%s: seq_len %lld not divisible by %s %lld", name, (long long)seq_len,
+                    zigzag ? "2*cp_size =" : "cp_size", (long long)div);
+    if (heads % cp_size != 0)
+        return fail(CPATTN_ERR_SHAPE, "%s: heads %d not divisible by cp_size %d", name, heads, cp_size);
+    const int64_t seg_bytes = (int64_t)(heads / cp_size) * head_dim * elem_bytes;
+    const int64_t span_bytes = seq_len / cp_size * seg_bytes;
+    if (span_bytes >= (1LL << 31) || (int64_t)cp_size * batch > 65535)
+        return fail(CPATTN_ERR_UNSUPPORTED, "%s: one shard's head group exceeds 2 GiB or "
+                                            "cp_size*batch exceeds 65535", name);
+    return from_hip(cpattn::launch_ulysses_permute(in, out, elem_bytes, batch, seq_len, heads, head_dim,
+                                                   cp_size, group, (int32_t)dir, zigzag, (hipStream_t)stream),
+                    name);
+}
+
+}  // namespace
+
 CPATTN_API cpattn_status_t cpattn_ulysses_permute(const void* in, void* out, int32_t elem_bytes,
                                                   int32_t batch, int64_t seq_len, int32_t heads,
                                                   int32_t head_dim, int32_t cp_size, int32_t group,
                                                   cpattn_permute_dir_t dir, void* stream) {
-    if (elem_bytes <= 0 || batch <= 0 || seq_len <= 0 || heads <= 0 || head_dim <= 0 || cp_size <= 0)
-        return fail(CPATTN_ERR_INVALID_ARG, "ulysses_permute: sizes must be > 0");
-    if (dir != CPATTN_SEQ_TO_HEADS && dir != CPATTN_HEADS_TO_SEQ)
-        return fail(CPATTN_ERR_INVALID_ARG, "ulysses_permute: unknown direction %d", (int)dir);
-    if (group < 0 || group >= cp_size)
-        return fail(CPATTN_ERR_INVALID_ARG, "ulysses_permute: group %d outside [0, %d)", group, cp_size);
-    if (!in || !out) return fail(CPATTN_ERR_INVALID_ARG, "ulysses_permute: NULL pointer");
-    if (in == out) return fail(CPATTN_ERR_INVALID_ARG, "ulysses_permute: in and out must differ");
-    if (seq_len % cp_size != 0)
-        return fail(CPATTN_ERR_SHAPE, "ulysses_permute: seq_len %lld not divisible by cp_size %d",
-                    (long long)seq_len, cp_size);
-    if (heads % cp_size != 0)
-        return fail(CPATTN_ERR_SHAPE, "ulysses_permute: heads %d not divisible by cp_size %d", heads,
-                    cp_size);
-    const int64_t seg_bytes = (int64_t)(heads / cp_size) * head_dim * elem_bytes;
-    const int64_t span_bytes = seq_len / cp_size * seg_bytes;
-    if (span_bytes >= (1LL << 31) || (int64_t)cp_size * batch > 65535)
-        return fail(CPATTN_ERR_UNSUPPORTED, "ulysses_permute: one shard's head group exceeds 2 GiB or "
-                                            "cp_size*batch exceeds 65535");
-    return from_hip(cpattn::launch_ulysses_permute(in, out, elem_bytes, batch, seq_len, heads, head_dim,
-                                                   cp_size, group, (int32_t)dir, (hipStream_t)stream),
-                    "ulysses_permute");
+    return ulysses_common("ulysses_permute", false, in, out, elem_bytes, batch, seq_len, heads, head_dim,
+                          cp_size, group, dir, stream);
+}
+
+CPATTN_API cpattn_status_t cpattn_ulysses_permute_zigzag(const void* in, void* out, int32_t elem_bytes,
+                                                         int32_t batch, int64_t seq_len, int32_t heads,
+                                                         int32_t head_dim, int32_t cp_size, int32_t group,
+                                                         cpattn_permute_dir_t dir, void* stream) {
+    return ulysses_common("ulysses_permute_zigzag", true, in, out, elem_bytes, batch, seq_len, heads,
+                          head_dim, cp_size, group, dir, stream);
 }

@@ -21,7 +21,8 @@ hipError_t launch_reorder_gathered(const void* in, void* out, int32_t batch, int
 
 hipError_t launch_ulysses_permute(const void* in, void* out, int32_t elem_bytes, int32_t batch,
                                   int64_t seq_len, int32_t heads, int32_t head_dim,
-                                  int32_t cp_size, int32_t group, int32_t dir, hipStream_t stream);
+                                  int32_t cp_size, int32_t group, int32_t dir, bool zigzag,
+                                  hipStream_t stream);
 
 struct BlockFwdArgs {
     const void* q;

@@ -4,6 +4,13 @@
 // parallelism: Ring Attention and Ulysses", section Ulysses: group g = heads
 // [g*H/C, (g+1)*H/C), and sequence shard src supplies rows [src*S/C, (src+1)*S/C).
 //
+// Zigzag shards (rank src holds chunks src and 2C-1-src of t = S/(2C) tokens, "On Context
+// Parallelism", section All-gather): the same exchange with the chunk reorder folded in, so
+// that the grouped tensor comes out in global sequence order ("On Context Parallelism",
+// section All-to-all: the gathered sequence is in rank order and must be put back in order
+// before causal attention).  Shard row i < t goes to global row src*t + i, row i >= t to
+// (2C-1-src)*t + i - t.
+//
 // For one (src, b) pair the move is a 2-D copy of s = S/C rows of one head-group segment
 // (H/C * D * elem bytes): in the stacked shards [C][B][S/C][H][D] the rows are H*D*elem
 // apart, in the grouped tensor [B][S][H/C][D] they are packed.  grid.y enumerates (src, b),
@@ -40,11 +47,12 @@ template <typename T>
 __global__ void __launch_bounds__(kThreads) ulysses_kernel(const T* __restrict__ in, T* __restrict__ out,
                                                            uint32_t span, FastDiv seg, int64_t row,
                                                            int64_t head_off, int64_t S, int64_t s,
-                                                           int64_t B, int32_t dir) {
+                                                           int64_t B, int32_t dir, int64_t zz_t,
+                                                           int64_t zz_last) {
     const int64_t sb = blockIdx.y;          // src * B + b
     const int64_t src = sb / B, b = sb - src * B;
     const int64_t stacked_base = sb * s * row + head_off;          // row i at + i*row
-    const int64_t grouped_base = (b * S + src * s) * (int64_t)seg.d;  // row i at + i*seg
+    const int64_t grouped_b = b * S * (int64_t)seg.d;
     const uint32_t base = blockIdx.x * (uint32_t)(kThreads * kVecPerThread) + threadIdx.x;
 #pragma unroll
     for (int u = 0; u < kVecPerThread; ++u) {
@@ -52,8 +60,11 @@ __global__ void __launch_bounds__(kThreads) ulysses_kernel(const T* __restrict__
         if (e >= span) break;
         const uint32_t i = fast_div(e, seg);
         const uint32_t w = e - i * seg.d;
+        // destination row: contiguous shards keep their order; zigzag shards split in two
+        const int64_t grow = (zz_t == 0) ? src * s + i
+                             : ((int64_t)i < zz_t ? src * zz_t + i : (zz_last - src) * zz_t + (i - zz_t));
         const int64_t so = stacked_base + (int64_t)i * row + w;
-        const int64_t go = grouped_base + e;
+        const int64_t go = grouped_b + grow * (int64_t)seg.d + w;
         if (dir == 0) out[go] = in[so];
         else out[so] = in[go];
     }
@@ -63,7 +74,8 @@ __global__ void __launch_bounds__(kThreads) ulysses_kernel(const T* __restrict__
 
 hipError_t launch_ulysses_permute(const void* in, void* out, int32_t elem_bytes, int32_t batch,
                                   int64_t seq_len, int32_t heads, int32_t head_dim,
-                                  int32_t cp_size, int32_t group, int32_t dir, hipStream_t stream) {
+                                  int32_t cp_size, int32_t group, int32_t dir, bool zigzag,
+                                  hipStream_t stream) {
     const int64_t hg = heads / cp_size;
     const int64_t seg_bytes = hg * head_dim * (int64_t)elem_bytes;
     const int64_t row_bytes = (int64_t)heads * head_dim * elem_bytes;
@@ -77,14 +89,16 @@ hipError_t launch_ulysses_permute(const void* in, void* out, int32_t elem_bytes,
     const int64_t per_block = kThreads * kVecPerThread;
     const dim3 grid((unsigned)((span + per_block - 1) / per_block), (unsigned)(cp_size * batch));
     const FastDiv fd = make_fastdiv((uint32_t)seg);
+    const int64_t zz_t = zigzag ? seq_len / (2 * (int64_t)cp_size) : 0;
+    const int64_t zz_last = 2 * (int64_t)cp_size - 1;
     if (vec)
         hipLaunchKernelGGL(ulysses_kernel<uint4>, grid, dim3(kThreads), 0, stream, (const uint4*)in,
                            (uint4*)out, (uint32_t)span, fd, row_bytes / el, off_bytes / el, seq_len,
-                           s, (int64_t)batch, dir);
+                           s, (int64_t)batch, dir, zz_t, zz_last);
     else
         hipLaunchKernelGGL(ulysses_kernel<uint8_t>, grid, dim3(kThreads), 0, stream,
                            (const uint8_t*)in, (uint8_t*)out, (uint32_t)span, fd, row_bytes,
-                           off_bytes, seq_len, s, (int64_t)batch, dir);
+                           off_bytes, seq_len, s, (int64_t)batch, dir, zz_t, zz_last);
     return hipGetLastError();
 }
 

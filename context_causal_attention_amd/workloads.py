@@ -1,4 +1,4 @@
-"""The five synthetic workloads the library is checked and measured on.
+"""The synthetic workloads the library is checked and measured on.
 
 Each is a rank's (or head group's) share of causal attention under context parallelism,
 with the shapes the pages work with: zigzag sharding with C=4 ("On Context Parallelism",
@@ -16,7 +16,7 @@ from dataclasses import dataclass
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str          # "ring_share" | "allgather" | "ulysses"
+    kind: str          # "ring_share" | "allgather" | "ulysses" | "usp"
     batch: int
     seq_len: int
     heads_q: int
@@ -24,8 +24,10 @@ class Workload:
     head_dim: int
     dtype: str         # "fp32" | "bf16"
     cp_size: int
-    rank: int | None = None    # ring_share: the rank whose share is computed (None: every rank)
+    rank: int | None = None    # ring_share, usp: the rank whose share is computed (None: every rank)
     group: int | None = None   # ulysses: the head group
+    a2a: int | None = None     # usp: all-to-all group size A (ring size R = C / A)
+    zigzag: bool = False       # ulysses: zigzag shards (the exchange folds in the chunk reorder)
 
     @property
     def chunk_len(self) -> int:
@@ -47,6 +49,13 @@ class Workload:
         t, C = self.chunk_len, self.cp_size
         return 2 * C * t * t + t
 
+    def usp_pairs_per_head(self) -> int:
+        """A mesh rank's share: its A2A group's tokens form rank g's zigzag shard over R,
+        so per query head of its group it sees 2R t'^2 + t' pairs with t' = S/(2R)."""
+        R = self.cp_size // self.a2a
+        t2 = self.seq_len // (2 * R)
+        return 2 * R * t2 * t2 + t2
+
     def causal_pairs_per_head(self) -> int:
         S = self.seq_len
         return S * (S + 1) // 2
@@ -60,5 +69,10 @@ WORKLOADS = {
         Workload("allgather_32k", "allgather", 1, 32768, 32, 32, 128, "bf16", 4, rank=None),
         Workload("ulysses_gqa_128k", "ulysses", 1, 131072, 32, 8, 128, "bf16", 8, group=3),
         Workload("ring_share_256k", "ring_share", 1, 262144, 32, 8, 128, "bf16", 8, rank=3),
+        # zigzag-sharded Ulysses (exchange with the chunk reorder folded in) and one rank of
+        # the two-dimensional mesh ("On Context Parallelism", "Peer-to-peer + All-to-all":
+        # C = 8 as A = 2 times R = 4; rank 3 is ring position 1, head group 1)
+        Workload("ulysses_zz_128k", "ulysses", 1, 131072, 32, 8, 128, "bf16", 8, group=3, zigzag=True),
+        Workload("usp_128k", "usp", 1, 131072, 32, 8, 128, "bf16", 8, rank=3, a2a=2),
     )
 }

@@ -207,6 +207,28 @@ cpattn_status_t cpattn_ulysses_permute(const void* in, void* out, int32_t elem_b
                                        int32_t head_dim, int32_t cp_size, int32_t group,
                                        cpattn_permute_dir_t dir, void* stream);
 
+/*
+ * cpattn_ulysses_permute_zigzag -- cpattn_ulysses_permute for zigzag shards, with the chunk
+ * reorder folded in so that the grouped side is in global sequence order.  Rank src holds
+ * chunks src and 2C-1-src of t = S/(2C) tokens ([CP] "All-gather"); the all-to-all
+ * concatenates shards in rank order, which causal attention cannot use until the chunks are
+ * put back in order ([CP] "All-to-all", [CP] "All-gather" for the rank-order layout).
+ * With C = A this is also the per-group exchange of the two-dimensional mesh of [CP]
+ * "Peer-to-peer + All-to-all": an A2A group's A zigzag shards come out as the group's
+ * tokens in increasing position order.
+ *
+ *   CPATTN_SEQ_TO_HEADS: in = stacked [C][B][S/C][H][D], out = [B][S][H/C][D] with
+ *                        out[b][p][h][d] = in[src][b][i][g*H/C + h][d] where shard row
+ *                        i < t holds position p = src*t + i and row i >= t holds
+ *                        p = (2C-1-src)*t + (i - t)
+ *   CPATTN_HEADS_TO_SEQ: the inverse; writes only group g's heads of the stacked out.
+ * Bit-exact.  Errors as for cpattn_ulysses_permute, and SHAPE if seq_len % (2*C) != 0.
+ */
+cpattn_status_t cpattn_ulysses_permute_zigzag(const void* in, void* out, int32_t elem_bytes,
+                                              int32_t batch, int64_t seq_len, int32_t heads,
+                                              int32_t head_dim, int32_t cp_size, int32_t group,
+                                              cpattn_permute_dir_t dir, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

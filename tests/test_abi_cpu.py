@@ -136,3 +136,14 @@ def test_block_fwd_merge_validation(lib):
     assert bfm(lse=NULL) == INVALID
     assert bfm(out=ctypes.c_void_p(0x1004)) == UNSUPPORTED
     assert bfm(seq_q=0, q=NULL, out=NULL, lse=NULL, qpos=NULL) == OK
+
+
+def test_ulysses_zigzag_validation(lib):
+    f = lib.cpattn_ulysses_permute_zigzag
+    other = ctypes.c_void_p(0x2000)
+    # seq_len must split into 2C chunks
+    assert f(FAKE, other, 2, 1, 36, 8, 16, 4, 0, 0, NULL) == SHAPE and "2*cp_size" in _err(lib)
+    assert f(FAKE, other, 2, 1, 32, 6, 16, 4, 0, 0, NULL) == SHAPE
+    assert f(FAKE, other, 2, 1, 32, 8, 16, 4, 4, 0, NULL) == INVALID
+    assert f(FAKE, FAKE, 2, 1, 32, 8, 16, 4, 0, 0, NULL) == INVALID
+    assert f(FAKE, other, 2, 1, 32, 8, 16, 4, 0, 7, NULL) == INVALID
