@@ -14,6 +14,9 @@ the pages step by step:
 * ``closed_form_share``: the same blocks folded at once with the boxed combine of
   "Context parallelism -- splitting the sequence across GPUs", section "How do partial
   softmax results combine?".
+* ``ring_rank_share_bwd``: the ring backward of "On Context Parallelism", section
+  "Peer-to-peer" / "Backward": per step the block backward of the local queries against
+  owner (rank - step) mod C's shard, dq summed over the steps, dk and dv kept per owner.
 * the zigzag Ulysses exchange (the all-to-all's rank-order concatenation followed by the
   chunk reorder) and the two-dimensional mesh of "On Context Parallelism", section
   "Peer-to-peer + All-to-all" (group positions, rank coordinates, the group's share).
@@ -69,9 +72,11 @@ def _load():
                                   P, P, P]
     L.orc_merge.argtypes = [P, P, P, P, i32, i64, i32, i32]
     L.orc_combine_blocks.argtypes = [P, P, P, i32, i64, i32, P, P]
+    L.orc_block_bwd.argtypes = [P, P, P, P, P, P, i32, i64, i64, i32, i32, i32, P, P, f64, P, i64, P,
+                                i64, P, P, P, i32]
     for name in ("orc_zigzag_positions", "orc_contiguous_positions", "orc_gathered_positions",
                  "orc_reorder", "orc_ulysses_permute", "orc_attention_rows", "orc_block_stats",
-                 "orc_merge", "orc_combine_blocks"):
+                 "orc_merge", "orc_combine_blocks", "orc_block_bwd"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -233,6 +238,30 @@ def combine_blocks(m, l, z):
     return out, lse
 
 
+def block_bwd(q, k, v, dout, out, lse, q_pos, kv_pos, scale: float, qrows=None, krows=None,
+              nthreads: int | None = None):
+    """Backward of one block (see ``orc_block_bwd``): returns (dq, dk, dv) in fp64 for the
+    selected query rows (default all) and key rows (default all).  out and lse are the
+    complete forward results of the query rows (fp64 or fp32 values)."""
+    q, k, v, dout = _f32(q), _f32(k), _f32(v), _f32(dout)
+    out = np.ascontiguousarray(out, dtype=np.float64)
+    lse = np.ascontiguousarray(lse, dtype=np.float64)
+    B, Sq, Hq, D = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    qp = np.ascontiguousarray(q_pos, dtype=np.int64)
+    kp = np.ascontiguousarray(kv_pos, dtype=np.int64)
+    qr = np.arange(Sq, dtype=np.int64) if qrows is None else np.ascontiguousarray(qrows, dtype=np.int64)
+    kr = np.arange(Skv, dtype=np.int64) if krows is None else np.ascontiguousarray(krows, dtype=np.int64)
+    dq = np.empty((B, len(qr), Hq, D))
+    dk = np.empty((B, len(kr), Hkv, D))
+    dv = np.empty((B, len(kr), Hkv, D))
+    _check(_load().orc_block_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(out), _ptr(lse), B, Sq, Skv,
+                                 Hq, Hkv, D, _ptr(qp), _ptr(kp), float(scale), _ptr(qr), len(qr), _ptr(kr),
+                                 len(kr), _ptr(dq), _ptr(dk), _ptr(dv),
+                                 nthreads or default_threads()), "block_bwd")
+    return dq, dk, dv
+
+
 # ----------------------------------------------------------------------------------------
 # The ring, emulated step by step ("On Context Parallelism", "Peer-to-peer" / "Forward")
 # ----------------------------------------------------------------------------------------
@@ -263,6 +292,26 @@ def ring_rank_share(q_local, k_full, v_full, S: int, C: int, r: int, scale: floa
         else:
             out, lse = merge(out, lse, t_out, t_lse)
     return out, lse, blocks
+
+
+def ring_rank_share_bwd(q_local, k_full, v_full, dout_local, out_local, lse_local, S: int, C: int,
+                        r: int, scale: float, layout: str = "zigzag"):
+    """Rank r's share of the ring backward: step i runs the block backward of the local
+    queries against owner (r - i) mod C's shard with the saved (complete) out and lse;
+    dq adds up over the steps, and each owner's dk, dv contribution is what travels with
+    its K/V.  Returns (dq_local, {owner: (dk_o, dv_o)}) with dk_o, dv_o in the owner's
+    local order."""
+    q_pos = owner_positions(S, C, r, layout)
+    dq = None
+    contrib = {}
+    for step in range(C):
+        owner = (r - step) % C
+        kv_pos = owner_positions(S, C, owner, layout)
+        t_dq, t_dk, t_dv = block_bwd(q_local, np.asarray(k_full)[:, kv_pos], np.asarray(v_full)[:, kv_pos],
+                                     dout_local, out_local, lse_local, q_pos, kv_pos, scale)
+        dq = t_dq if dq is None else dq + t_dq
+        contrib[owner] = (t_dk, t_dv)
+    return dq, contrib
 
 
 def closed_form_share(q_local, k_full, v_full, S: int, C: int, r: int, scale: float,

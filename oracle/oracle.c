@@ -319,3 +319,126 @@ int orc_combine_blocks(const double* m, const double* l, const double* z, int32_
     }
     return ORC_OK;
 }
+
+/* ------------------------------------------------------------------------------------ */
+/* Backward of one block.  [CP] section "Peer-to-peer" / "Backward": each ring step takes  */
+/* the local queries, one K/V block, the saved output and lse and the output gradient,    */
+/* and yields tile_dq, tile_dk, tile_dv; dq adds up over the steps and dk, dv over the     */
+/* ranks.  The pages do not print the formulas; they are the chain rule applied to the     */
+/* attention definition above.  With lse_i the row's complete log-sum-exp (all blocks):    */
+/*   p_ij  = exp(scale <q_i, k_j> - lse_i) for visible pairs, 0 otherwise                  */
+/*   D_i   = sum_d dout_i,d out_i,d                                                         */
+/*   dp_ij = <dout_i, v_j>,   ds_ij = p_ij (dp_ij - D_i)                                    */
+/*   dq_i  = scale sum_j ds_ij k_j,  dk_j = scale sum_i ds_ij q_i,  dv_j = sum_i p_ij dout_i */
+/* Grouped-query attention: dk and dv of kv head c sum over the query heads reading it.    */
+/* Layouts: q, dout [B][Sq][Hq][D]; k, v [B][Skv][Hkv][D] (fp32 values); out [B][Sq][Hq][D] */
+/* and lse [B][Hq][Sq] fp64.  Outputs for the selected query rows qrows and key rows krows: */
+/* dq [B][nq][Hq][D], dk and dv [B][nk][Hkv][D], fp64, overwritten.                        */
+/* ------------------------------------------------------------------------------------ */
+typedef struct {
+    const float *q, *k, *v, *dout;
+    const double *out, *lse;
+    int64_t B, Sq, Skv, Hq, Hkv, D;
+    const int64_t *qpos, *kvpos, *qrows, *krows;
+    int64_t nq, nk;
+    double scale;
+    double *dq, *dk, *dv;
+    int64_t next;
+    pthread_mutex_t mu;
+} bwd_job_t;
+
+static double bwd_delta(const bwd_job_t* J, int64_t b, int64_t h, int64_t i) {
+    const float* g = J->dout + ((b * J->Sq + i) * J->Hq + h) * J->D;
+    const double* o = J->out + ((b * J->Sq + i) * J->Hq + h) * J->D;
+    double s = 0.0;
+    for (int64_t d = 0; d < J->D; ++d) s += (double)g[d] * o[d];
+    return s;
+}
+
+/* p_ij and ds_ij of one visible pair (query row i of head h, key row j of kv head c) */
+static void bwd_pair(const bwd_job_t* J, int64_t b, int64_t h, int64_t i, int64_t c, int64_t j,
+                     double delta, double* p, double* ds) {
+    const int64_t D = J->D;
+    const float* qi = J->q + ((b * J->Sq + i) * J->Hq + h) * D;
+    const float* gi = J->dout + ((b * J->Sq + i) * J->Hq + h) * D;
+    const float* kj = J->k + ((b * J->Skv + j) * J->Hkv + c) * D;
+    const float* vj = J->v + ((b * J->Skv + j) * J->Hkv + c) * D;
+    double s = 0.0, dp = 0.0;
+    for (int64_t d = 0; d < D; ++d) {
+        s += (double)qi[d] * (double)kj[d];
+        dp += (double)gi[d] * (double)vj[d];
+    }
+    *p = exp(s * J->scale - J->lse[(b * J->Hq + h) * J->Sq + i]);
+    *ds = *p * (dp - delta);
+}
+
+static void* bwd_worker(void* arg) {
+    bwd_job_t* J = (bwd_job_t*)arg;
+    const int64_t D = J->D, G = J->Hq / J->Hkv;
+    const int64_t nq_jobs = J->B * J->Hq * J->nq, total = nq_jobs + J->B * J->Hkv * J->nk;
+    for (;;) {
+        pthread_mutex_lock(&J->mu);
+        const int64_t w = J->next++;
+        pthread_mutex_unlock(&J->mu);
+        if (w >= total) break;
+        if (w < nq_jobs) {
+            /* dq of one query row */
+            const int64_t ri = w % J->nq, h = (w / J->nq) % J->Hq, b = w / (J->nq * J->Hq);
+            const int64_t i = J->qrows[ri], c = h / G;
+            double* dq = J->dq + ((b * J->nq + ri) * J->Hq + h) * D;
+            for (int64_t d = 0; d < D; ++d) dq[d] = 0.0;
+            if (J->lse[(b * J->Hq + h) * J->Sq + i] == -INFINITY) continue;
+            const double delta = bwd_delta(J, b, h, i);
+            for (int64_t j = 0; j < J->Skv; ++j) {
+                if (J->kvpos[j] > J->qpos[i]) continue;
+                double p, ds;
+                bwd_pair(J, b, h, i, c, j, delta, &p, &ds);
+                const float* kj = J->k + ((b * J->Skv + j) * J->Hkv + c) * D;
+                for (int64_t d = 0; d < D; ++d) dq[d] += J->scale * ds * (double)kj[d];
+            }
+        } else {
+            /* dk and dv of one key row */
+            const int64_t u = w - nq_jobs;
+            const int64_t rj = u % J->nk, c = (u / J->nk) % J->Hkv, b = u / (J->nk * J->Hkv);
+            const int64_t j = J->krows[rj];
+            double* dk = J->dk + ((b * J->nk + rj) * J->Hkv + c) * D;
+            double* dv = J->dv + ((b * J->nk + rj) * J->Hkv + c) * D;
+            for (int64_t d = 0; d < D; ++d) { dk[d] = 0.0; dv[d] = 0.0; }
+            for (int64_t h = c * G; h < (c + 1) * G; ++h)
+                for (int64_t i = 0; i < J->Sq; ++i) {
+                    if (J->kvpos[j] > J->qpos[i]) continue;
+                    if (J->lse[(b * J->Hq + h) * J->Sq + i] == -INFINITY) continue;
+                    double p, ds;
+                    bwd_pair(J, b, h, i, c, j, bwd_delta(J, b, h, i), &p, &ds);
+                    const float* qi = J->q + ((b * J->Sq + i) * J->Hq + h) * D;
+                    const float* gi = J->dout + ((b * J->Sq + i) * J->Hq + h) * D;
+                    for (int64_t d = 0; d < D; ++d) {
+                        dk[d] += J->scale * ds * (double)qi[d];
+                        dv[d] += p * (double)gi[d];
+                    }
+                }
+        }
+    }
+    return NULL;
+}
+
+int orc_block_bwd(const float* q, const float* k, const float* v, const float* dout, const double* out,
+                  const double* lse, int32_t B, int64_t Sq, int64_t Skv, int32_t Hq, int32_t Hkv, int32_t D,
+                  const int64_t* qpos, const int64_t* kvpos, double scale, const int64_t* qrows,
+                  int64_t nq, const int64_t* krows, int64_t nk, double* dq, double* dk, double* dv,
+                  int32_t nthreads) {
+    if (B <= 0 || Sq < 0 || Skv < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv != 0) return ORC_BAD;
+    if (nq < 0 || nk < 0) return ORC_BAD;
+    for (int64_t r = 0; r < nq; ++r) if (qrows[r] < 0 || qrows[r] >= Sq) return ORC_BAD;
+    for (int64_t r = 0; r < nk; ++r) if (krows[r] < 0 || krows[r] >= Skv) return ORC_BAD;
+    bwd_job_t J = {q, k, v, dout, out, lse, B, Sq, Skv, Hq, Hkv, D, qpos, kvpos, qrows, krows,
+                   nq, nk, scale, dq, dk, dv, 0};
+    pthread_mutex_init(&J.mu, NULL);
+    if (nthreads < 1) nthreads = 1;
+    pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    for (int32_t t = 0; t < nthreads; ++t) pthread_create(&th[t], NULL, bwd_worker, &J);
+    for (int32_t t = 0; t < nthreads; ++t) pthread_join(th[t], NULL);
+    free(th);
+    pthread_mutex_destroy(&J.mu);
+    return ORC_OK;
+}
