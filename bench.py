@@ -32,6 +32,8 @@ ROOT = Path(__file__).resolve().parent
 sys.path.insert(0, str(ROOT))
 
 METRIC = "causal attn TFLOP/s per rank share (unmasked FLOPs) + % of bf16 MFMA peak"
+METRIC_BWD = ("causal attn backward TFLOP/s per rank share (10*D FLOPs per unmasked pair and query "
+              "head) + % of bf16 MFMA peak")
 PEAK_BF16_TFLOPS = 2500.0   # MI355X published dense bf16 matrix peak
 PEAK_FP32_TFLOPS = 157.3    # MI355X published fp32 vector peak
 PEAK_HBM_GBS = 8000.0       # MI355X published HBM3E bandwidth
@@ -44,6 +46,9 @@ def parse_args(argv=None):
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="ring_share_256k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
+                    help="bwd: time the ring-share backward (delta + one block backward per ring "
+                         "step) instead of the forward; ring_share workloads only")
     ap.add_argument("--unfused", action="store_true",
                     help="ring share: write each step's tile and merge it with the separate merge kernel")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -57,7 +62,7 @@ def parse_args(argv=None):
 class Plan:
     """Buffers and the launch sequence of one step of a workload."""
 
-    def __init__(self, w, dev, fused=True):
+    def __init__(self, w, dev, fused=True, backward=False):
         import torch
         import context_causal_attention_amd as cp
         from context_causal_attention_amd import synthetic
@@ -157,6 +162,23 @@ class Plan:
                 self.attn_flops.append(4.0 * w.batch * hq * w.head_dim * pairs)
         else:
             raise ValueError(w.kind)
+        self.backward = False
+        if backward:
+            if w.kind != "ring_share" or w.rank is None:
+                raise ValueError("--pass bwd needs a ring_share workload with a rank")
+            # the saved forward state comes from this library's forward, run once here
+            r = w.rank
+            self.step()
+            torch.cuda.synchronize()
+            self.dout = synthetic.chunks("dout", [r, 2 * C - 1 - r], heads=w.heads_q, **kw).to(dev)
+            self.dq = torch.empty_like(self.out)
+            self.dks = [torch.empty(k.shape, dtype=torch.float32, device=dev) for k in self.k]
+            self.dvs = [torch.empty(v.shape, dtype=torch.float32, device=dev) for v in self.v]
+            self.delta = torch.empty_like(self.lse)
+            # algorithmic backward FLOPs: 10*D per visible pair and query head (S = QK^T
+            # recomputed, dP = dO V^T, dV = P^T dO, dQ = dS K, dK = dS^T Q)
+            self.attn_flops = [f * 2.5 for f in self.attn_flops]
+            self.backward = True
         self.flops = sum(self.attn_flops)
 
     def step(self, ev=None):
@@ -164,6 +186,8 @@ class Plan:
         pairs around each block attention launch are appended."""
         cp, torch, w = self.cp, self.torch, self.w
         C = w.cp_size
+        if getattr(self, "backward", False):
+            return self.step_bwd(ev)
 
         def attn(*a, fn=cp.block_fwd):
             if ev is not None:
@@ -221,6 +245,28 @@ class Plan:
                 else:
                     attn(*a_, self.out, self.lse, fn=cp.block_fwd_merge)
             cp.ulysses_heads_to_seq(self.out, a, self.ost, zigzag=True)
+
+
+    def step_bwd(self, ev=None):
+        """One rank share of the ring backward: delta, then the block backward of each ring
+        step (dq written at step 0 and added after; each owner's dk, dv written by its step)."""
+        cp, torch, w = self.cp, self.torch, self.w
+        C, r = w.cp_size, w.rank
+        cp.attn_bwd_delta(self.out, self.dout, self.delta)
+        q = self.qs[r]
+        for step in range(C):
+            owner = (r - step) % C
+            flags = cp.BWD_WRITE_DKV | (cp.BWD_WRITE_DQ if step == 0 else 0)
+            a = (q, self.k[owner], self.v[owner], self.dout, self.pos[r], self.pos[owner], w.scale, self.lse,
+                 self.delta, self.dq, self.dks[owner], self.dvs[owner], flags)
+            if ev is not None:
+                s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                s.record()
+                cp.block_bwd(*a)
+                e.record()
+                ev.append((s, e))
+            else:
+                cp.block_bwd(*a)
 
 
 def profiled_traffic(workload: str, kernel: str):
@@ -317,7 +363,7 @@ def main(argv=None) -> int:
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    plan = Plan(w, dev, fused=not args.unfused)
+    plan = Plan(w, dev, fused=not args.unfused, backward=args.which == "bwd")
     if args.copy_calibration_mib > 0:
         import context_causal_attention_amd as cp
         n = args.copy_calibration_mib << 20
@@ -343,8 +389,11 @@ def main(argv=None) -> int:
     attn_flops = plan.attn_flops * args.steps
     achieved = sum(attn_flops) / (sum(attn_ms) * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    bwd = args.which == "bwd"
+    kernel = ("block_bwd_dq_kernel+block_bwd_dkdv_kernel" if bwd else "block_fwd_bf16_kernel") \
+        if w.dtype == "bf16" else ("bwd_dq_f32_kernel+bwd_dkdv_f32_kernel" if bwd else "block_fwd_f32_kernel")
     result = {
-        "metric": METRIC,
+        "metric": METRIC_BWD if bwd else METRIC,
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -356,18 +405,22 @@ def main(argv=None) -> int:
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic (seeded iid N(0,1), per-chunk generators)",
-        "config": {"workload": w.name + ("_unfused" if args.unfused and w.kind == "ring_share" else ""),
+        "config": {"workload": w.name + ("_unfused" if args.unfused and w.kind == "ring_share" else "")
+                   + ("_bwd" if bwd else ""),
                    "batch": w.batch, "a2a": w.a2a, "zigzag": w.zigzag, "seq_len": w.seq_len, "cp_size": w.cp_size,
                    "rank": w.rank, "group": w.group, "heads_q": w.heads_q, "heads_kv": w.heads_kv,
                    "head_dim": w.head_dim, "unmasked_flops_per_step": plan.flops},
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
-        "roofline": {"bound": "mfma", "kernel": "block_fwd_bf16_kernel" if w.dtype == "bf16" else "block_fwd_f32_kernel",
+        "roofline": {"bound": "mfma", "kernel": kernel,
                      "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4),
-                     "traffic": profiled_traffic(w.name, "block_fwd_bf16_kernel") if w.dtype == "bf16" else None,
+                     "traffic": profiled_traffic(w.name, "block_fwd_bf16_kernel") if w.dtype == "bf16" and not bwd
+                     else None,
                      "avg_launch_ms": round(sum(attn_ms) / len(attn_ms), 4), "launches": len(attn_ms)},
     }
-    if not args.no_cpu_baseline:
+    if bwd:
+        result["cpu_baseline"] = None  # the oracle baseline is quoted for the forward line
+    elif not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)
     return 0

@@ -6,11 +6,15 @@ layout companions of the all-gather and Ulysses variants.  This package is the t
 Python binding; build the library with ``python -m context_causal_attention_amd.build``.
 """
 from ._binding import (  # noqa: F401
+    BWD_WRITE_DKV,
+    BWD_WRITE_DQ,
     HEADS_TO_SEQ,
     RANK_TO_SEQ,
     SEQ_TO_HEADS,
     SEQ_TO_RANK,
     CpattnError,
+    attn_bwd_delta,
+    block_bwd,
     block_fwd,
     block_fwd_merge,
     header_entry_points,
@@ -18,6 +22,7 @@ from ._binding import (  # noqa: F401
     load_library,
     lse_merge,
     reorder_gathered,
+    ring_share_bwd,
     ring_share_fwd,
     ulysses_heads_to_seq,
     ulysses_seq_to_heads,

@@ -18,6 +18,7 @@ LIB_PATH = _PKG / "libcpattn.so"
 HEADER = _PKG.parent / "include" / "cpattn.h"
 
 CPATTN_F32, CPATTN_BF16 = 0, 1
+BWD_WRITE_DQ, BWD_WRITE_DKV = 1, 2
 RANK_TO_SEQ, SEQ_TO_RANK = 0, 1
 SEQ_TO_HEADS, HEADS_TO_SEQ = 0, 1
 STATUS = {0: "CPATTN_OK", 1: "CPATTN_ERR_INVALID_ARG", 2: "CPATTN_ERR_SHAPE",
@@ -55,10 +56,14 @@ def load_library():
     L.cpattn_block_fwd.argtypes = [P, P, P, ctypes.c_int, i32, i64, i64, i32, i32, i32, P, P, f32, P, P, P]
     L.cpattn_block_fwd_merge.argtypes = list(L.cpattn_block_fwd.argtypes)
     L.cpattn_lse_merge.argtypes = [P, P, P, P, i32, i64, i32, i32, P]
+    L.cpattn_attn_bwd_delta.argtypes = [P, P, ctypes.c_int, i32, i64, i32, i32, P, P]
+    L.cpattn_block_bwd.argtypes = [P, P, P, P, ctypes.c_int, i32, i64, i64, i32, i32, i32, P, P, f32, P, P, P,
+                                   P, P, ctypes.c_uint32, P]
     L.cpattn_reorder_gathered.argtypes = [P, P, i32, i64, i64, i32, ctypes.c_int, P]
     L.cpattn_ulysses_permute.argtypes = [P, P, i32, i32, i64, i32, i32, i32, i32, ctypes.c_int, P]
     L.cpattn_ulysses_permute_zigzag.argtypes = list(L.cpattn_ulysses_permute.argtypes)
     for name in ("cpattn_zigzag_index", "cpattn_block_fwd", "cpattn_block_fwd_merge", "cpattn_lse_merge",
+                 "cpattn_attn_bwd_delta", "cpattn_block_bwd",
                  "cpattn_reorder_gathered", "cpattn_ulysses_permute", "cpattn_ulysses_permute_zigzag"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
@@ -294,3 +299,70 @@ def usp_share_fwd(q_st: torch.Tensor, k_sts, v_sts, ring_rank: int, head_group: 
     out, lse = ring_share_fwd(qh, kh, vh, pos, ring_rank, scale)
     ulysses_heads_to_seq(out, head_group, out_st, zigzag=True)
     return out, lse
+
+
+def attn_bwd_delta(out: torch.Tensor, dout: torch.Tensor, delta: torch.Tensor | None = None) -> torch.Tensor:
+    """delta [B, H, S] = <dout, out> per row; out fp32 [B, S, H, D], dout bf16 or fp32."""
+    L = load_library()
+    B, S, H, D = out.shape
+    _need(out, "out", torch.float32)
+    _need(dout, "dout", None, (B, S, H, D))
+    if dout.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("dout must be bf16 or fp32")
+    if delta is None:
+        delta = torch.empty((B, H, S), dtype=torch.float32, device=out.device)
+    _need(delta, "delta", torch.float32, (B, H, S))
+    dt = CPATTN_BF16 if dout.dtype == torch.bfloat16 else CPATTN_F32
+    _check(L.cpattn_attn_bwd_delta(_ptr(out), _ptr(dout), dt, B, S, H, D, _ptr(delta), _stream(out.device)))
+    return delta
+
+
+def block_bwd(q, k, v, dout, q_pos, kv_pos, scale: float, lse, delta, dq, dk, dv, flags: int = 0):
+    """Backward of one block, added into dq [B, Sq, Hq, D], dk and dv [B, Skv, Hkv, D] (fp32);
+    ``flags`` BWD_WRITE_DQ / BWD_WRITE_DKV overwrite instead of adding."""
+    L = load_library()
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("q must be bf16 or fp32")
+    B, Sq, Hq, D = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    _need(q, "q")
+    _need(k, "k", q.dtype, (B, Skv, Hkv, D))
+    _need(v, "v", q.dtype, (B, Skv, Hkv, D))
+    _need(dout, "dout", q.dtype, (B, Sq, Hq, D))
+    _need(q_pos, "q_pos", torch.int64, (Sq,))
+    _need(kv_pos, "kv_pos", torch.int64, (Skv,))
+    _need(lse, "lse", torch.float32, (B, Hq, Sq))
+    _need(delta, "delta", torch.float32, (B, Hq, Sq))
+    _need(dq, "dq", torch.float32, (B, Sq, Hq, D))
+    _need(dk, "dk", torch.float32, (B, Skv, Hkv, D))
+    _need(dv, "dv", torch.float32, (B, Skv, Hkv, D))
+    dt = CPATTN_BF16 if q.dtype == torch.bfloat16 else CPATTN_F32
+    _check(L.cpattn_block_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), dt, B, Sq, Skv, Hq, Hkv, D, _ptr(q_pos),
+                              _ptr(kv_pos), float(scale), _ptr(lse), _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv),
+                              int(flags), _stream(q.device)))
+    return dq, dk, dv
+
+
+def ring_share_bwd(q, k_blocks, v_blocks, positions, rank: int, scale: float, out, lse, dout,
+                   dq=None, dk_blocks=None, dv_blocks=None):
+    """Rank ``rank``'s share of the ring backward ("On Context Parallelism", Peer-to-peer /
+    Backward): delta once, then for each step the block backward against owner
+    (rank - step) mod C's K/V; dq adds up over the steps, and owner o's dk and dv
+    contributions go into ``dk_blocks[o]``, ``dv_blocks[o]`` (the buffers that travel with
+    its K/V on a ring).  Step 0 writes dq and each owner's dk, dv are written by its one step,
+    so nothing needs clearing first.  Returns (dq, dk_blocks, dv_blocks)."""
+    C = len(k_blocks)
+    B, s, Hq, D = q.shape
+    if dq is None:
+        dq = torch.empty((B, s, Hq, D), dtype=torch.float32, device=q.device)
+    if dk_blocks is None:
+        dk_blocks = [torch.empty(k.shape, dtype=torch.float32, device=q.device) for k in k_blocks]
+    if dv_blocks is None:
+        dv_blocks = [torch.empty(v.shape, dtype=torch.float32, device=q.device) for v in v_blocks]
+    delta = attn_bwd_delta(out, dout)
+    for step in range(C):
+        owner = (rank - step) % C
+        flags = BWD_WRITE_DKV | (BWD_WRITE_DQ if step == 0 else 0)
+        block_bwd(q, k_blocks[owner], v_blocks[owner], dout, positions[rank], positions[owner], scale, lse,
+                  delta, dq, dk_blocks[owner], dv_blocks[owner], flags)
+    return dq, dk_blocks, dv_blocks

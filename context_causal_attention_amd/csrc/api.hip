@@ -139,6 +139,82 @@ CPATTN_API cpattn_status_t cpattn_block_fwd_merge(const void* q, const void* k, 
                             heads_kv, head_dim, q_positions, kv_positions, scale, out, lse, stream);
 }
 
+CPATTN_API cpattn_status_t cpattn_attn_bwd_delta(const float* out, const void* dout, cpattn_dtype_t dtype,
+                                                 int32_t batch, int64_t seq, int32_t heads, int32_t head_dim,
+                                                 float* delta, void* stream) {
+    if (dtype != CPATTN_F32 && dtype != CPATTN_BF16)
+        return fail(CPATTN_ERR_INVALID_ARG, "attn_bwd_delta: unknown dtype %d", (int)dtype);
+    if (batch <= 0 || heads <= 0 || head_dim <= 0)
+        return fail(CPATTN_ERR_INVALID_ARG, "attn_bwd_delta: batch, heads and head_dim must be > 0");
+    if (seq < 0) return fail(CPATTN_ERR_INVALID_ARG, "attn_bwd_delta: seq must be >= 0");
+    if (seq == 0) return ok();
+    if (!out || !dout || !delta) return fail(CPATTN_ERR_INVALID_ARG, "attn_bwd_delta: NULL pointer");
+    if (head_dim % 4 != 0)
+        return fail(CPATTN_ERR_SHAPE, "attn_bwd_delta: head_dim %d not a multiple of 4", head_dim);
+    if (!aligned16(out)) return fail(CPATTN_ERR_UNSUPPORTED, "attn_bwd_delta: out must be 16-byte aligned");
+    if (((int64_t)batch * seq * heads * 16 + 255) / 256 > kMaxGrid)
+        return fail(CPATTN_ERR_UNSUPPORTED, "attn_bwd_delta: launch grid too large");
+    return from_hip(cpattn::launch_attn_bwd_delta(out, dout, dtype == CPATTN_BF16, batch, seq, heads, head_dim,
+                                                  delta, (hipStream_t)stream),
+                    "attn_bwd_delta");
+}
+
+CPATTN_API cpattn_status_t cpattn_block_bwd(const void* q, const void* k, const void* v, const void* dout,
+                                            cpattn_dtype_t dtype, int32_t batch, int64_t seq_q, int64_t seq_kv,
+                                            int32_t heads_q, int32_t heads_kv, int32_t head_dim,
+                                            const int64_t* q_positions, const int64_t* kv_positions,
+                                            float scale, const float* lse, const float* delta, float* dq,
+                                            float* dk, float* dv, uint32_t flags, void* stream) {
+    const char* name = "block_bwd";
+    if (flags & ~(uint32_t)(CPATTN_BWD_WRITE_DQ | CPATTN_BWD_WRITE_DKV))
+        return fail(CPATTN_ERR_INVALID_ARG, "%s: unknown flags 0x%x", name, flags);
+    const bool wdq = (flags & CPATTN_BWD_WRITE_DQ) != 0, wdkv = (flags & CPATTN_BWD_WRITE_DKV) != 0;
+    if (dtype != CPATTN_F32 && dtype != CPATTN_BF16)
+        return fail(CPATTN_ERR_INVALID_ARG, "%s: unknown dtype %d", name, (int)dtype);
+    if (batch <= 0 || heads_q <= 0 || heads_kv <= 0)
+        return fail(CPATTN_ERR_INVALID_ARG, "%s: batch and head counts must be > 0", name);
+    if (seq_q < 0 || seq_kv < 0)
+        return fail(CPATTN_ERR_INVALID_ARG, "%s: sequence lengths must be >= 0", name);
+    if (!(scale > 0.f) || !isfinite(scale))
+        return fail(CPATTN_ERR_INVALID_ARG, "%s: scale must be finite and > 0", name);
+    if (heads_q % heads_kv != 0)
+        return fail(CPATTN_ERR_SHAPE, "%s: heads_q %d not a multiple of heads_kv %d", name, heads_q, heads_kv);
+    if (head_dim != 64 && head_dim != 128)
+        return fail(CPATTN_ERR_UNSUPPORTED, "%s: head_dim %d (supported: 64, 128)", name, head_dim);
+    if (dtype == CPATTN_BF16 && head_dim != 128)
+        return fail(CPATTN_ERR_UNSUPPORTED, "%s: bf16 path supports head_dim 128 only", name);
+    if (seq_q == 0 || seq_kv == 0) {
+        // no pair: nothing to add; accumulators to overwrite become zero
+        if (wdq && seq_q > 0) {
+            if (!dq) return fail(CPATTN_ERR_INVALID_ARG, "%s: NULL pointer", name);
+            const hipError_t e = cpattn::launch_zero_fill(dq, (int64_t)batch * seq_q * heads_q * head_dim,
+                                                          (hipStream_t)stream);
+            if (e != hipSuccess) return from_hip(e, name);
+        }
+        if (wdkv && seq_kv > 0) {
+            if (!dk || !dv) return fail(CPATTN_ERR_INVALID_ARG, "%s: NULL pointer", name);
+            const int64_t n = (int64_t)batch * seq_kv * heads_kv * head_dim;
+            hipError_t e = cpattn::launch_zero_fill(dk, n, (hipStream_t)stream);
+            if (e == hipSuccess) e = cpattn::launch_zero_fill(dv, n, (hipStream_t)stream);
+            if (e != hipSuccess) return from_hip(e, name);
+        }
+        return ok();
+    }
+    if (!q || !k || !v || !dout || !q_positions || !kv_positions || !lse || !delta || !dq || !dk || !dv)
+        return fail(CPATTN_ERR_INVALID_ARG, "%s: NULL pointer", name);
+    if (dtype == CPATTN_BF16 && (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) ||
+                                 !aligned16(dq) || !aligned16(dk) || !aligned16(dv)))
+        return fail(CPATTN_ERR_UNSUPPORTED, "%s: bf16 path needs 16-byte aligned q, k, v, dout, dq, dk, dv", name);
+    if ((seq_q + 31) / 32 * (int64_t)batch * heads_q > kMaxGrid ||
+        (seq_kv + 31) / 32 * (int64_t)batch * heads_kv > kMaxGrid || heads_q > 65535 || batch > 65535)
+        return fail(CPATTN_ERR_UNSUPPORTED, "%s: launch grid too large", name);
+    cpattn::BlockBwdArgs a{q,  k,     v,     dout,   q_positions, kv_positions, lse,      delta, dq, dk,
+                           dv, batch, seq_q, seq_kv, heads_q,     heads_kv,     head_dim, scale, wdq, wdkv};
+    const hipError_t e = (dtype == CPATTN_BF16) ? cpattn::launch_block_bwd_bf16(a, (hipStream_t)stream)
+                                                : cpattn::launch_block_bwd_f32(a, (hipStream_t)stream);
+    return from_hip(e, name);
+}
+
 CPATTN_API cpattn_status_t cpattn_lse_merge(float* out, float* lse, const float* out_tile,
                                             const float* lse_tile, int32_t batch, int64_t seq,
                                             int32_t heads, int32_t head_dim, void* stream) {

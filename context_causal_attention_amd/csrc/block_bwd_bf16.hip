@@ -1,0 +1,637 @@
+// bf16 attention backward of one block on the gfx950 matrix cores.
+//
+// What it computes ("On Context Parallelism", section Peer-to-peer / Backward: each ring step
+// yields tile_dq, tile_dk, tile_dv of the local queries against one K/V block from the saved
+// output and lse; the formulas are the chain rule of the attention definition):
+//   p_ij = exp(scale <q_i,k_j> - lse_i) on visible pairs, D_i = <dout_i, out_i> (given),
+//   ds_ij = p_ij (<dout_i, v_j> - D_i),
+//   dq_i += scale sum_j ds_ij k_j,  dk_j += scale sum_i ds_ij q_i,  dv_j += sum_i p_ij dout_i.
+// lse is the row's complete log-sum-exp, so p is the global softmax weight and the blocks'
+// contributions add up to the whole gradient.
+//
+// Two kernels, each with bf16 matrix-core products (v_mfma_f32_32x32x16_bf16) and fp32
+// accumulation; p and ds are rounded to bf16 (RNE) before the products that consume them.
+//
+// dq kernel: a block of 4 waves owns G query heads sharing one K/V head times 128/G query
+// positions; each lane holds one query row (its q and dout as matrix operands).  K/V tiles
+// of 64 keys are staged in LDS (direct global->LDS loads, two stages).  Per tile:
+//   S^T = K Q^T and dP^T = V dO^T (K, V rows read from LDS), p and ds per lane (one query:
+//   lse and D are per-lane scalars), dQ^T += K^T dS^T (K read transposed, ds_read_b64_tr_b16).
+// dk/dv kernel: a block of 4 waves owns 128 keys of one K/V head (32 per wave, one per lane,
+// k and v as matrix operands) and walks the query tiles of 64 rows that see them, for every
+// query head of the group.  Q, dO, lse and D tiles are staged in LDS.  Per 32-query half:
+//   S = Q K^T and dP = dO V^T (Q, dO rows from LDS), p and ds (lse and D per accumulator
+//   row, read from LDS), dV^T += dO^T P and dK^T += Q^T dS (Q, dO read transposed).
+// The causal structure is used as in the forward: tiles entirely hidden are skipped, tiles
+// entirely visible need no mask, and partly visible tiles compare row indices with a count
+// found once by binary search over the positions.
+#include "cpattn_internal.h"
+
+#include <math.h>
+
+namespace cpattn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+#define LDS_AS __attribute__((address_space(3)))
+#define GLOBAL_AS __attribute__((address_space(1)))
+
+constexpr int kD = 128;
+constexpr int kRowBytes = kD * 2;
+constexpr int kTile = 64;                   // keys (dq kernel) or queries (dk/dv kernel) per tile
+constexpr int kTileBytes = kTile * kRowBytes;
+constexpr int kNW = 4;                      // waves per block
+constexpr int kThreads = 64 * kNW;
+constexpr int kRowsPerWave = kTile / kNW;   // tile rows each wave loads
+constexpr int kLoads = kRowsPerWave / 4;    // 16-byte loads per lane per tensor and tile
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct BwdParams {
+    const __bf16* q;
+    const __bf16* k;
+    const __bf16* v;
+    const __bf16* dout;
+    const int64_t* qpos;
+    const int64_t* kvpos;
+    const float* lse;
+    const float* delta;
+    float* dq;
+    float* dk;
+    float* dv;
+    int64_t seq_q;
+    int64_t seq_kv;
+    int32_t batch;
+    int32_t heads_q;
+    int32_t heads_kv;
+    int32_t ratio;      // heads_q / heads_kv
+    float c;            // scale * log2(e)
+    float scale;
+    // dq grid: G query heads per block, pq positions, n_hg head groups, n_cols columns
+    int32_t G;
+    int32_t pq;
+    int32_t n_hg;
+    int32_t n_cols;
+    int64_t n_qt;
+    int32_t xcd_cols;
+    // dk/dv grid: key blocks of 128 keys, columns (b, kv head)
+    int64_t n_kb;
+    int32_t kv_cols;
+    int32_t kv_xcd_cols;
+    int32_t write_dq;   // overwrite instead of adding
+    int32_t write_dkv;
+};
+
+__device__ inline int wave_sum(int x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+
+__device__ inline bf16x8 lds_b128(const LDS_AS char* p) { return *(const LDS_AS bf16x8*)p; }
+
+__device__ inline bf16x8 lds_tr_pair(const LDS_AS char* p0, const LDS_AS char* p1) {
+    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)p0);
+    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)p1);
+    const s16x8 c = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return __builtin_bit_cast(bf16x8, c);
+}
+
+__device__ inline void load_lds16(const void* g, LDS_AS void* lds_base) {
+    __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)g, lds_base, 16, 0, 0);
+}
+
+__device__ inline bf16x8 load_row16(const __bf16* p, bool valid) {
+    const u32x4 raw = valid ? *(const u32x4*)p : u32x4{0, 0, 0, 0};
+    return __builtin_bit_cast(bf16x8, raw);
+}
+
+__device__ inline f32x16 mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Tiles in LDS are row-major (256 bytes per row) with 16-byte chunk c of row r stored at
+// chunk c ^ (r & 15): row reads of 16 consecutive rows are conflict-free, and transposed reads
+// of 4 rows by 16-lane groups stay within two passes.
+//
+// Row-read offsets (matrix-core A operand, 32 rows x 16 columns, lane = row l32 holding
+// columns 16*ks + 8*half .. +7): row l32 of a 32-row block.
+__device__ inline uint32_t row_off(int lane, int ks) {
+    const int l32 = lane & 31, half = lane >> 5;
+    return l32 * kRowBytes + (((2 * ks + half) ^ (lane & 15)) << 4);
+}
+// Transposed-read offsets (A operand = columns 32*db .. +31 as rows, 16 tile rows as k): the
+// k order is the accumulator's row order 16*ks2 + 8*(j/4) + 4*half + j%4, so that an operand
+// packed straight from an accumulator lines up.  Two 8-byte reads per operand: tile rows
+// vkey and vkey + 8 of the 16-row step.
+struct TrOff {
+    uint32_t a, b;
+};
+__device__ inline TrOff tr_off(int lane, int db) {
+    const int half = lane >> 5, grp = lane >> 4, s16 = lane & 15;
+    const int vkey = 4 * half + (s16 >> 2);
+    const int chunk = 4 * db + 2 * (grp & 1) + ((s16 & 3) >> 1);
+    const uint32_t lo = (s16 & 1) << 3;
+    return TrOff{vkey * kRowBytes + ((chunk ^ vkey) << 4) + lo,
+                 (vkey + 8) * kRowBytes + ((chunk ^ (vkey + 8)) << 4) + lo};
+}
+
+// ------------------------------------------------------------------------------------------
+// dq kernel
+// ------------------------------------------------------------------------------------------
+__global__ void __launch_bounds__(kThreads, 1) block_bwd_dq_kernel(const BwdParams p) {
+    __shared__ __attribute__((aligned(16))) char lds_stage0[2 * kTileBytes];  // [K|V]
+    __shared__ __attribute__((aligned(16))) char lds_stage1[2 * kTileBytes];
+    __shared__ int red[2 * kNW];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const int half = lane >> 5;
+    const int l32 = lane & 31;
+
+    int col;
+    int64_t qt_rank;
+    if (p.xcd_cols > 0) {
+        const int x = blockIdx.x & 7;
+        const int64_t kk = blockIdx.x >> 3;
+        qt_rank = kk / p.xcd_cols;
+        col = x + 8 * (int)(kk % p.xcd_cols);
+    } else {
+        col = (int)(blockIdx.x % p.n_cols);
+        qt_rank = blockIdx.x / p.n_cols;
+    }
+    const int64_t qt = p.n_qt - 1 - qt_rank;  // late queries (most keys) first
+    const int hg = col % p.n_hg;
+    const int kvh = (col / p.n_hg) % p.heads_kv;
+    const int64_t b = col / (p.n_hg * p.heads_kv);
+
+    const int64_t q0 = qt * p.pq;
+    const int64_t q_last = (q0 + p.pq < p.seq_q ? q0 + p.pq : p.seq_q) - 1;
+    const int64_t pmin = p.qpos[q0];
+    const int64_t pmax = p.qpos[q_last];
+
+    // visible key tiles (a prefix) and tiles visible to every query of the block
+    const int64_t n_tiles = (p.seq_kv + kTile - 1) / kTile;
+    int c_ne = 0, c_full = 0;
+    for (int64_t t = tid; t < n_tiles; t += kThreads) {
+        c_ne += (p.kvpos[t * kTile] <= pmax) ? 1 : 0;
+        const int64_t lk = t * kTile + kTile - 1;
+        c_full += (lk < p.seq_kv && p.kvpos[lk] <= pmin) ? 1 : 0;
+    }
+    c_ne = wave_sum(c_ne);
+    c_full = wave_sum(c_full);
+    if (lane == 0) {
+        red[w] = c_ne;
+        red[kNW + w] = c_full;
+    }
+    __syncthreads();
+    int n_ne = 0, n_full = 0;
+#pragma unroll
+    for (int i = 0; i < kNW; ++i) {
+        n_ne += red[i];
+        n_full += red[kNW + i];
+    }
+
+    // K/V tile loads (both tensors row-read, same swizzle)
+    const int64_t kvstride = (int64_t)p.heads_kv * kD;
+    const char* kbase = (const char*)(p.k + (b * p.seq_kv * p.heads_kv + kvh) * (int64_t)kD);
+    const char* vbase = (const char*)(p.v + (b * p.seq_kv * p.heads_kv + kvh) * (int64_t)kD);
+    const int64_t tile_bytes_g = (int64_t)kTile * kvstride * 2;
+    const int ld_row_in = lane >> 4;
+    const int ld_chunk = lane & 15;
+    uint32_t koff[kLoads];
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+        const int row = w * kRowsPerWave + 4 * i + ld_row_in;
+        koff[i] = (uint32_t)(row * kvstride * 2) + ((ld_chunk ^ (row & 15)) << 4);
+    }
+    auto issue_tile = [&](int jt, LDS_AS char* kt) {
+        LDS_AS char* vt = kt + kTileBytes;
+        const char* kb_t = kbase + (int64_t)jt * tile_bytes_g;
+        const char* vb_t = vbase + (int64_t)jt * tile_bytes_g;
+        const int64_t rmax = p.seq_kv - 1 - (int64_t)jt * kTile;  // last valid row of the tile
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) {
+            const int row = w * kRowsPerWave + 4 * i + ld_row_in;
+            // rows past the end re-read the last key (finite data the mask hides)
+            const uint32_t back = (row > rmax) ? (uint32_t)((row - rmax) * kvstride * 2) : 0u;
+            load_lds16(kb_t + koff[i] - back, kt + (w * kRowsPerWave + 4 * i) * kRowBytes);
+            load_lds16(vb_t + koff[i] - back, vt + (w * kRowsPerWave + 4 * i) * kRowBytes);
+        }
+    };
+
+    // this lane's query row: q and dout as B operands, lse (log2 domain) and D as scalars
+    const int row0 = w * 32;
+    const int hs = row0 / p.pq;
+    const int64_t i = q0 + (row0 % p.pq) + l32;
+    const int64_t head = (int64_t)kvh * p.ratio + (int64_t)hg * p.G + hs;
+    const bool valid = i < p.seq_q;
+    const int64_t mypos = valid ? p.qpos[i] : INT64_MIN;
+    const int64_t qrow = (b * p.seq_q + (valid ? i : 0)) * p.heads_q + head;
+    bf16x8 qreg[kD / 16], doreg[kD / 16];
+#pragma unroll
+    for (int ks = 0; ks < kD / 16; ++ks) {
+        qreg[ks] = load_row16(p.q + qrow * kD + 16 * ks + 8 * half, valid);
+        doreg[ks] = load_row16(p.dout + qrow * kD + 16 * ks + 8 * half, valid);
+    }
+    const int64_t li = (b * p.heads_q + head) * p.seq_q + (valid ? i : 0);
+    const float lse_v = valid ? p.lse[li] : INFINITY;
+    // a row with no visible key anywhere has lse = -inf and every pair masked
+    const float lse2 = (lse_v == -INFINITY) ? INFINITY : lse_v * kLog2e;
+    const float dlt = valid ? p.delta[li] : 0.f;
+
+    int64_t vis = 0;  // keys visible to this row, needed only when some tile is partly visible
+    if (n_full < n_ne) {
+        int64_t lo = (int64_t)n_full * kTile;
+        int64_t hi = (int64_t)n_ne * kTile < p.seq_kv ? (int64_t)n_ne * kTile : p.seq_kv;
+        while (lo < hi) {
+            const int64_t mid = (lo + hi) >> 1;
+            if (p.kvpos[mid] <= mypos) lo = mid + 1; else hi = mid;
+        }
+        vis = lo;
+    }
+
+    f32x16 acc[kD / 32];
+#pragma unroll
+    for (int db = 0; db < kD / 32; ++db) acc[db] = f32x16{};
+
+    uint32_t off_r[kD / 16];
+#pragma unroll
+    for (int ks = 0; ks < kD / 16; ++ks) off_r[ks] = row_off(lane, ks);
+    TrOff off_t[kD / 32];
+#pragma unroll
+    for (int db = 0; db < kD / 32; ++db) off_t[db] = tr_off(lane, db);
+
+    LDS_AS char* st0 = (LDS_AS char*)lds_stage0;
+    LDS_AS char* st1 = (LDS_AS char*)lds_stage1;
+
+    auto tile = [&](int jt, const LDS_AS char* kt, LDS_AS char* nxt) {
+        const LDS_AS char* vt = kt + kTileBytes;
+        if (jt + 1 < n_ne) issue_tile(jt + 1, nxt);
+
+        // S^T = K Q^T and dP^T = V dO^T for the tile's two 32-key blocks
+        f32x16 s[2], dp[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            s[kb] = f32x16{};
+            dp[kb] = f32x16{};
+        }
+#pragma unroll
+        for (int ks = 0; ks < kD / 16; ++ks)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const bf16x8 ka = lds_b128(kt + kb * 32 * kRowBytes + off_r[ks]);
+                const bf16x8 va = lds_b128(vt + kb * 32 * kRowBytes + off_r[ks]);
+                s[kb] = mfma(ka, qreg[ks], s[kb]);
+                dp[kb] = mfma(va, doreg[ks], dp[kb]);
+            }
+
+        // ds = p (dp - D); entry v of key block kb is key 32*kb + 8*(v/4) + 4*half + v%4
+        const bool masked = jt >= n_full;
+        const int64_t rel = vis - (int64_t)jt * kTile - 4 * half;
+        const int lim = rel < 0 ? 0 : (rel > kTile ? kTile : (int)rel);
+        bf16x8 dsb[2][2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][v], p.c, -lse2));
+                if (masked && 32 * kb + 8 * (v / 4) + v % 4 >= lim) pv = 0.f;
+                dsb[kb][v >> 3][v & 7] = (__bf16)(pv * (dp[kb][v] - dlt));
+            }
+
+        // dQ^T += K^T dS^T
+#pragma unroll
+        for (int db = 0; db < kD / 32; ++db)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int ks2 = 0; ks2 < 2; ++ks2) {
+                    const LDS_AS char* base = kt + (32 * kb + 16 * ks2) * kRowBytes;
+                    const bf16x8 a = lds_tr_pair(base + off_t[db].a, base + off_t[db].b);
+                    acc[db] = mfma(a, dsb[kb][ks2], acc[db]);
+                }
+
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next tile has landed
+        __syncthreads();
+    };
+
+    if (n_ne > 0) issue_tile(0, st0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    for (int jt = 0; jt < n_ne; jt += 2) {
+        tile(jt, st0, st1);
+        if (jt + 1 < n_ne) tile(jt + 1, st1, st0);
+    }
+
+    // dq += scale * dQ; accumulator entry v of block db is dimension 32*db + 8*(v/4) + 4*half + v%4
+    if (!valid) return;
+    float* drow = p.dq + qrow * kD;
+#pragma unroll
+    for (int db = 0; db < kD / 32; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            float4* dst = (float4*)(drow + 32 * db + 8 * g + 4 * half);
+            float4 x = p.write_dq ? make_float4(0.f, 0.f, 0.f, 0.f) : *dst;
+            x.x += p.scale * acc[db][4 * g + 0];
+            x.y += p.scale * acc[db][4 * g + 1];
+            x.z += p.scale * acc[db][4 * g + 2];
+            x.w += p.scale * acc[db][4 * g + 3];
+            *dst = x;
+        }
+}
+
+// ------------------------------------------------------------------------------------------
+// dk/dv kernel
+// ------------------------------------------------------------------------------------------
+constexpr int kStageBytes = 2 * kTileBytes + 2 * kTile * 4;  // [Q | dO | lse2 | D]
+
+__global__ void __launch_bounds__(kThreads, 1) block_bwd_dkdv_kernel(const BwdParams p) {
+    __shared__ __attribute__((aligned(16))) char lds_stage0[kStageBytes];
+    __shared__ __attribute__((aligned(16))) char lds_stage1[kStageBytes];
+    __shared__ int red[2 * kNW];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const int half = lane >> 5;
+    const int l32 = lane & 31;
+
+    int col;
+    int64_t kb_rank;
+    if (p.kv_xcd_cols > 0) {
+        const int x = blockIdx.x & 7;
+        const int64_t kk = blockIdx.x >> 3;
+        kb_rank = kk / p.kv_xcd_cols;
+        col = x + 8 * (int)(kk % p.kv_xcd_cols);
+    } else {
+        col = (int)(blockIdx.x % p.kv_cols);
+        kb_rank = blockIdx.x / p.kv_cols;
+    }
+    const int64_t kblk = kb_rank;  // early keys (most queries) first
+    const int kvh = col % p.heads_kv;
+    const int64_t b = col / p.heads_kv;
+
+    const int64_t k0 = kblk * (32 * kNW);
+    const int64_t k_last = (k0 + 32 * kNW < p.seq_kv ? k0 + 32 * kNW : p.seq_kv) - 1;
+    const int64_t kmin = p.kvpos[k0];
+    const int64_t kmax = p.kvpos[k_last];
+
+    // query tiles that see some key of the block (a suffix, from qt_lo) and tiles whose every
+    // query sees every key of the block (a shorter suffix, from qt_full)
+    const int64_t n_qt = (p.seq_q + kTile - 1) / kTile;
+    int c_hidden = 0, c_part = 0;
+    for (int64_t t = tid; t < n_qt; t += kThreads) {
+        const int64_t lq = (t * kTile + kTile - 1 < p.seq_q) ? t * kTile + kTile - 1 : p.seq_q - 1;
+        c_hidden += (p.qpos[lq] < kmin) ? 1 : 0;
+        c_part += (p.qpos[t * kTile] < kmax) ? 1 : 0;
+    }
+    c_hidden = wave_sum(c_hidden);
+    c_part = wave_sum(c_part);
+    if (lane == 0) {
+        red[w] = c_hidden;
+        red[kNW + w] = c_part;
+    }
+    __syncthreads();
+    int qt_lo = 0, qt_full = 0;
+#pragma unroll
+    for (int ii = 0; ii < kNW; ++ii) {
+        qt_lo += red[ii];
+        qt_full += red[kNW + ii];
+    }
+    const int nq_vis = (int)n_qt - qt_lo;
+    const int n_steps = nq_vis > 0 ? nq_vis * p.ratio : 0;  // (query head, query tile) pairs
+    const int64_t h0 = (int64_t)kvh * p.ratio;
+
+    // this lane's key row: k and v as B operands
+    const int64_t key = k0 + w * 32 + l32;
+    const bool kvalid = key < p.seq_kv;
+    const int64_t krow = (b * p.seq_kv + (kvalid ? key : 0)) * p.heads_kv + kvh;
+    bf16x8 kreg[kD / 16], vreg[kD / 16];
+#pragma unroll
+    for (int ks = 0; ks < kD / 16; ++ks) {
+        kreg[ks] = load_row16(p.k + krow * kD + 16 * ks + 8 * half, kvalid);
+        vreg[ks] = load_row16(p.v + krow * kD + 16 * ks + 8 * half, kvalid);
+    }
+    // first query row that sees this key (rows before it are masked), when some tile is partial
+    int64_t first = 0;
+    if (qt_lo < qt_full) {
+        const int64_t kp = kvalid ? p.kvpos[key] : INT64_MAX;
+        int64_t lo = (int64_t)qt_lo * kTile;
+        int64_t hi = (int64_t)qt_full * kTile < p.seq_q ? (int64_t)qt_full * kTile : p.seq_q;
+        while (lo < hi) {
+            const int64_t mid = (lo + hi) >> 1;
+            if (p.qpos[mid] < kp) lo = mid + 1; else hi = mid;
+        }
+        first = kvalid ? lo : INT64_MAX;
+    }
+
+    // Q/dO tile loads: step u is query head h0 + u / nq_vis, query tile qt_lo + u % nq_vis
+    const int64_t qstride = (int64_t)p.heads_q * kD;
+    const int64_t qtile_bytes_g = (int64_t)kTile * qstride * 2;
+    const int ld_row_in = lane >> 4;
+    const int ld_chunk = lane & 15;
+    uint32_t qoff[kLoads];
+#pragma unroll
+    for (int ii = 0; ii < kLoads; ++ii) {
+        const int row = w * kRowsPerWave + 4 * ii + ld_row_in;
+        qoff[ii] = (uint32_t)(row * qstride * 2) + ((ld_chunk ^ (row & 15)) << 4);
+    }
+    auto step_of = [&](int u, int64_t& h, int64_t& qt) {
+        h = h0 + u / nq_vis;
+        qt = qt_lo + u % nq_vis;
+    };
+    auto issue_tile = [&](int u, LDS_AS char* st) {
+        int64_t h, qt;
+        step_of(u, h, qt);
+        const char* qb_t = (const char*)(p.q + (b * p.seq_q * p.heads_q + h) * (int64_t)kD) + qt * qtile_bytes_g;
+        const char* gb_t = (const char*)(p.dout + (b * p.seq_q * p.heads_q + h) * (int64_t)kD) + qt * qtile_bytes_g;
+        const int64_t rmax = p.seq_q - 1 - qt * kTile;
+#pragma unroll
+        for (int ii = 0; ii < kLoads; ++ii) {
+            const int row = w * kRowsPerWave + 4 * ii + ld_row_in;
+            // rows past the end re-read the last query; their lse is +inf, so p = 0
+            const uint32_t back = (row > rmax) ? (uint32_t)((row - rmax) * qstride * 2) : 0u;
+            load_lds16(qb_t + qoff[ii] - back, st + (w * kRowsPerWave + 4 * ii) * kRowBytes);
+            load_lds16(gb_t + qoff[ii] - back, st + kTileBytes + (w * kRowsPerWave + 4 * ii) * kRowBytes);
+        }
+    };
+    // lse (log2 domain, +inf past the end or for rows with no visible key) and D of a step,
+    // one value per thread of the first two waves, fetched a step ahead through registers
+    auto fetch_rowvals = [&](int u) -> float {
+        int64_t h, qt;
+        step_of(u, h, qt);
+        const int r = tid & 63;
+        const int64_t row = qt * kTile + r;
+        if (tid >= 2 * kTile) return 0.f;
+        const int64_t li = (b * p.heads_q + h) * p.seq_q + row;
+        if (tid < kTile) {
+            const float l = (row < p.seq_q) ? p.lse[li] : INFINITY;
+            return (l == -INFINITY) ? INFINITY : l * kLog2e;
+        }
+        return (row < p.seq_q) ? p.delta[li] : 0.f;
+    };
+    auto store_rowvals = [&](LDS_AS char* st, float x) {
+        if (tid < 2 * kTile) ((LDS_AS float*)(st + 2 * kTileBytes))[tid] = x;
+    };
+
+    f32x16 dk[kD / 32], dv[kD / 32];
+#pragma unroll
+    for (int db = 0; db < kD / 32; ++db) {
+        dk[db] = f32x16{};
+        dv[db] = f32x16{};
+    }
+    uint32_t off_r[kD / 16];
+#pragma unroll
+    for (int ks = 0; ks < kD / 16; ++ks) off_r[ks] = row_off(lane, ks);
+    TrOff off_t[kD / 32];
+#pragma unroll
+    for (int db = 0; db < kD / 32; ++db) off_t[db] = tr_off(lane, db);
+
+    LDS_AS char* st0 = (LDS_AS char*)lds_stage0;
+    LDS_AS char* st1 = (LDS_AS char*)lds_stage1;
+
+    auto step = [&](int u, const LDS_AS char* st, LDS_AS char* nxt) {
+        const LDS_AS char* qt_l = st;
+        const LDS_AS char* gt_l = st + kTileBytes;
+        const LDS_AS float* lse_l = (const LDS_AS float*)(st + 2 * kTileBytes);
+        const LDS_AS float* dlt_l = lse_l + kTile;
+        float nextv = 0.f;
+        if (u + 1 < n_steps) {
+            issue_tile(u + 1, nxt);
+            nextv = fetch_rowvals(u + 1);
+        }
+        int64_t h, qt;
+        step_of(u, h, qt);
+        const bool masked = qt < qt_full;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys
+            f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < kD / 16; ++ks) {
+                const bf16x8 qa = lds_b128(qt_l + qb * 32 * kRowBytes + off_r[ks]);
+                const bf16x8 ga = lds_b128(gt_l + qb * 32 * kRowBytes + off_r[ks]);
+                s = mfma(qa, kreg[ks], s);
+                dp = mfma(ga, vreg[ks], dp);
+            }
+            // entry v is query row qb*32 + 8*(v/4) + 4*half + v%4 of the tile, key l32
+            const int64_t rel = first - qt * kTile - qb * 32 - 4 * half;
+            const int lim = rel < 0 ? 0 : (rel > 32 ? 32 : (int)rel);
+            bf16x8 pb[2], dsb[2];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int r0 = qb * 32 + 8 * g + 4 * half;
+                const f32x4 lv = *(const LDS_AS f32x4*)(lse_l + r0);
+                const f32x4 dv4 = *(const LDS_AS f32x4*)(dlt_l + r0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int v = 4 * g + e;
+                    float pv = __builtin_amdgcn_exp2f(fmaf(s[v], p.c, -lv[e]));
+                    if (masked && 8 * g + e < lim) pv = 0.f;
+                    pb[v >> 3][v & 7] = (__bf16)pv;
+                    dsb[v >> 3][v & 7] = (__bf16)(pv * (dp[v] - dv4[e]));
+                }
+            }
+            // dV^T += dO^T P and dK^T += Q^T dS
+#pragma unroll
+            for (int db = 0; db < kD / 32; ++db)
+#pragma unroll
+                for (int ks2 = 0; ks2 < 2; ++ks2) {
+                    const int rb = (qb * 32 + 16 * ks2) * kRowBytes;
+                    const bf16x8 ga = lds_tr_pair(gt_l + rb + off_t[db].a, gt_l + rb + off_t[db].b);
+                    const bf16x8 qa = lds_tr_pair(qt_l + rb + off_t[db].a, qt_l + rb + off_t[db].b);
+                    dv[db] = mfma(ga, pb[ks2], dv[db]);
+                    dk[db] = mfma(qa, dsb[ks2], dk[db]);
+                }
+        }
+        // every wave is done with this stage; the next one (tiles and row values) is in place
+        if (u + 1 < n_steps) store_rowvals(nxt, nextv);
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+    };
+
+    if (n_steps > 0) {
+        issue_tile(0, st0);
+        store_rowvals(st0, fetch_rowvals(0));
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    for (int u = 0; u < n_steps; u += 2) {
+        step(u, st0, st1);
+        if (u + 1 < n_steps) step(u + 1, st1, st0);
+    }
+
+    // dk += scale * dK, dv += dV; entry v of block db is dimension 32*db + 8*(v/4) + 4*half + v%4
+    if (!kvalid) return;
+    float* krow_k = p.dk + krow * kD;
+    float* krow_v = p.dv + krow * kD;
+#pragma unroll
+    for (int db = 0; db < kD / 32; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            float4* dst = (float4*)(krow_k + 32 * db + 8 * g + 4 * half);
+            float4 x = p.write_dkv ? make_float4(0.f, 0.f, 0.f, 0.f) : *dst;
+            x.x += p.scale * dk[db][4 * g + 0];
+            x.y += p.scale * dk[db][4 * g + 1];
+            x.z += p.scale * dk[db][4 * g + 2];
+            x.w += p.scale * dk[db][4 * g + 3];
+            *dst = x;
+            float4* dsv = (float4*)(krow_v + 32 * db + 8 * g + 4 * half);
+            float4 y = p.write_dkv ? make_float4(0.f, 0.f, 0.f, 0.f) : *dsv;
+            y.x += dv[db][4 * g + 0];
+            y.y += dv[db][4 * g + 1];
+            y.z += dv[db][4 * g + 2];
+            y.w += dv[db][4 * g + 3];
+            *dsv = y;
+        }
+}
+
+}  // namespace
+
+hipError_t launch_block_bwd_bf16(const BlockBwdArgs& a, hipStream_t stream) {
+    BwdParams p;
+    p.q = (const __bf16*)a.q;
+    p.k = (const __bf16*)a.k;
+    p.v = (const __bf16*)a.v;
+    p.dout = (const __bf16*)a.dout;
+    p.qpos = a.q_pos;
+    p.kvpos = a.kv_pos;
+    p.lse = a.lse;
+    p.delta = a.delta;
+    p.dq = a.dq;
+    p.dk = a.dk;
+    p.dv = a.dv;
+    p.seq_q = a.seq_q;
+    p.seq_kv = a.seq_kv;
+    p.batch = a.batch;
+    p.heads_q = a.heads_q;
+    p.heads_kv = a.heads_kv;
+    p.ratio = a.heads_q / a.heads_kv;
+    p.c = a.scale * kLog2e;
+    p.scale = a.scale;
+    p.G = (p.ratio % 4 == 0) ? 4 : (p.ratio % 2 == 0) ? 2 : 1;
+    p.n_hg = p.ratio / p.G;
+    p.n_cols = a.batch * a.heads_kv * p.n_hg;
+    p.xcd_cols = (p.n_cols % 8 == 0) ? p.n_cols / 8 : 0;
+    p.pq = 32 * kNW / p.G;
+    p.n_qt = (a.seq_q + p.pq - 1) / p.pq;
+    p.n_kb = (a.seq_kv + 32 * kNW - 1) / (32 * kNW);
+    p.kv_cols = a.batch * a.heads_kv;
+    p.kv_xcd_cols = (p.kv_cols % 8 == 0) ? p.kv_cols / 8 : 0;
+    p.write_dq = a.write_dq ? 1 : 0;
+    p.write_dkv = a.write_dkv ? 1 : 0;
+    hipLaunchKernelGGL(block_bwd_dq_kernel, dim3((unsigned)(p.n_qt * p.n_cols)), dim3(kThreads), 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(block_bwd_dkdv_kernel, dim3((unsigned)(p.n_kb * p.kv_cols)), dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace cpattn

@@ -51,4 +51,36 @@ hipError_t launch_block_fwd_f32(const BlockFwdArgs& a, hipStream_t stream);
 // bf16 inputs, bf16 matrix-core products with fp32 accumulation.
 hipError_t launch_block_fwd_bf16(const BlockFwdArgs& a, hipStream_t stream);
 
+struct BlockBwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* dout;
+    const int64_t* q_pos;
+    const int64_t* kv_pos;
+    const float* lse;
+    const float* delta;
+    float* dq;
+    float* dk;
+    float* dv;
+    int32_t batch;
+    int64_t seq_q;
+    int64_t seq_kv;
+    int32_t heads_q;
+    int32_t heads_kv;
+    int32_t head_dim;
+    float scale;
+    bool write_dq;   // overwrite dq instead of adding to it
+    bool write_dkv;  // overwrite dk and dv instead of adding to them
+};
+
+// delta[b][h][i] = <dout[b][i][h], out[b][i][h]> (dout bf16 or fp32, out fp32).
+hipError_t launch_attn_bwd_delta(const float* out, const void* dout, bool bf16, int32_t batch, int64_t seq,
+                                 int32_t heads, int32_t head_dim, float* delta, hipStream_t stream);
+// One block's backward, accumulated into dq, dk, dv (fp32 and bf16 paths).
+hipError_t launch_block_bwd_f32(const BlockBwdArgs& a, hipStream_t stream);
+hipError_t launch_block_bwd_bf16(const BlockBwdArgs& a, hipStream_t stream);
+// n floats of p set to 0 (an accumulator that no block writes)
+hipError_t launch_zero_fill(float* p, int64_t n, hipStream_t stream);
+
 }  // namespace cpattn

@@ -4,7 +4,7 @@ This module only draws random numbers and rounds them to the storage dtype; it h
 of the attention, layout or merge arithmetic.  Both the HIP path (tests, bench) and the CPU
 oracle take their inputs from here, so the two see bit-identical values.
 
-Recipe: tensor ``name`` in {q, k, v} is drawn one sequence chunk at a time.  Chunk ``c``
+Recipe: tensor ``name`` in {q, k, v, dout} (dout: the output gradient of the backward) is drawn one sequence chunk at a time.  Chunk ``c``
 (tokens [c*chunk_len, (c+1)*chunk_len) of the global sequence) comes from
 ``torch.Generator().manual_seed(seed + 1_000_003 * tensor_id + c)`` as iid N(0, 1) fp32
 of shape [B, chunk_len, H, D], then rounded to the storage dtype (bf16 with
@@ -16,7 +16,7 @@ from concurrent.futures import ThreadPoolExecutor
 
 import torch
 
-TENSOR_IDS = {"q": 0, "k": 1, "v": 2}
+TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "dout": 3}
 SEED_STRIDE = 1_000_003
 
 

@@ -46,6 +46,10 @@ typedef enum {
 
 typedef enum { CPATTN_F32 = 0, CPATTN_BF16 = 1 } cpattn_dtype_t;
 
+/* flags of cpattn_block_bwd */
+#define CPATTN_BWD_WRITE_DQ 1u  /* dq = this block's part instead of dq += it */
+#define CPATTN_BWD_WRITE_DKV 2u /* the same for dk and dv */
+
 typedef enum {
     CPATTN_RANK_TO_SEQ = 0, /* all-gather (rank) order -> global sequence order */
     CPATTN_SEQ_TO_RANK = 1  /* global sequence order -> all-gather (rank) order */
@@ -167,6 +171,57 @@ cpattn_status_t cpattn_block_fwd_merge(const void* q, const void* k, const void*
 cpattn_status_t cpattn_lse_merge(float* out, float* lse, const float* out_tile,
                                  const float* lse_tile, int32_t batch, int64_t seq,
                                  int32_t heads, int32_t head_dim, void* stream);
+
+/*
+ * cpattn_attn_bwd_delta -- the row term of the attention backward, D_i = <dout_i, out_i>.
+ * [CP] "Peer-to-peer" / "Backward" (and "All-gather" / "Backward"): the backward of every
+ * ring step starts from the saved output and its gradient; the softmax derivative needs
+ * this per-row dot product (ds_ij = p_ij (dp_ij - D_i)), which is the same for all steps,
+ * so it is computed once per rank share.
+ *
+ *   out    in  fp32 [batch][seq][heads][head_dim] (the complete forward output)
+ *   dout   in  [batch][seq][heads][head_dim], dtype (bf16 or fp32)
+ *   delta  out fp32 [batch][heads][seq]
+ * Errors: INVALID_ARG (NULL pointer, sizes <= 0, seq < 0, bad dtype), SHAPE (head_dim % 4
+ * != 0), UNSUPPORTED (out not 16-byte aligned).  seq == 0 is a no-op.
+ */
+cpattn_status_t cpattn_attn_bwd_delta(const float* out, const void* dout, cpattn_dtype_t dtype,
+                                      int32_t batch, int64_t seq, int32_t heads, int32_t head_dim,
+                                      float* delta, void* stream);
+
+/*
+ * cpattn_block_bwd -- the backward of one block, ADDED into gradient accumulators.
+ * [CP] "Peer-to-peer" / "Backward": each ring step computes tile_dq, tile_dk, tile_dv of
+ * the local queries against one K/V block from the saved output and lse; dq accumulates
+ * locally over the steps, dk and dv accumulate in the buffers that travel with the block.
+ * With lse the complete (merged) log-sum-exp of each query row:
+ *   p_ij  = exp(scale <q_i, k_j> - lse_i)  for kv_positions[j] <= q_positions[i], else 0
+ *   ds_ij = p_ij (<dout_i, v_j> - delta_i)
+ *   dq_i += scale sum_j ds_ij k_j;  dk_j += scale sum_i ds_ij q_i;  dv_j += sum_i p_ij dout_i
+ * (chain rule of the attention definition of cpattn_block_fwd).  Grouped-query attention:
+ * dk, dv of kv head c sum over the query heads h with h / (heads_q/heads_kv) == c.
+ *
+ *   q, dout      in  [batch][seq_q][heads_q][head_dim], dtype
+ *   k, v         in  [batch][seq_kv][heads_kv][head_dim], dtype
+ *   positions    in  int64, strictly increasing (precondition, as for cpattn_block_fwd)
+ *   lse          in  fp32 [batch][heads_q][seq_q] (from the forward; -inf: no visible key)
+ *   delta        in  fp32 [batch][heads_q][seq_q] (cpattn_attn_bwd_delta)
+ *   dq           in/out fp32 [batch][seq_q][heads_q][head_dim]   (+= this block's part)
+ *   dk, dv       in/out fp32 [batch][seq_kv][heads_kv][head_dim] (+= this block's part)
+ *   flags        CPATTN_BWD_WRITE_DQ: dq = this block's part (no prior contents read);
+ *                CPATTN_BWD_WRITE_DKV: the same for dk and dv.  A ring share passes
+ *                WRITE_DQ on its first step, so no accumulator needs clearing.
+ * dtype CPATTN_BF16: bf16 products with fp32 accumulation; p and ds are rounded to bf16
+ * (RNE) before the products that use them.  CPATTN_F32: fp32 throughout.  head_dim 64 or
+ * 128 (bf16: 128).  seq_q == 0 or seq_kv == 0 adds nothing.
+ * Errors: INVALID_ARG (also unknown flag bits), SHAPE, UNSUPPORTED as for cpattn_block_fwd.
+ */
+cpattn_status_t cpattn_block_bwd(const void* q, const void* k, const void* v, const void* dout,
+                                 cpattn_dtype_t dtype, int32_t batch, int64_t seq_q, int64_t seq_kv,
+                                 int32_t heads_q, int32_t heads_kv, int32_t head_dim,
+                                 const int64_t* q_positions, const int64_t* kv_positions, float scale,
+                                 const float* lse, const float* delta, float* dq, float* dk, float* dv,
+                                 uint32_t flags, void* stream);
 
 /*
  * cpattn_reorder_gathered -- chunk reorder between the all-gather's rank order and the

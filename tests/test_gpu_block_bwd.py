@@ -1,0 +1,211 @@
+"""HIP attention backward against the oracle: the row term D, the block backward (both
+dtypes, GQA, every zigzag step class, sparse positions with empty rows, ragged tails), the
+write/accumulate flags, and the ring-share backward at the 8K and 256K workloads (sampled rows
+and keys, in the launch sequence the benchmark times; at 256K the saved forward state is
+synthetic, since the oracle cannot run that forward for every row).
+
+Tolerances: fp32, 1e-5 times max(1, largest reference magnitude).  bf16: p and ds are
+rounded to bf16 (relative error <= 2^-9 each) before the products that use them; on these
+inputs that moves a gradient by about 2^-9 of the largest entry, and the test allows 2^-7 of it."""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import context_causal_attention_amd as cp
+import oracle
+from context_causal_attention_amd.workloads import WORKLOADS
+from helpers import gen, max_abs, sample_rows, zigzag_chunks
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TDT = {"bf16": torch.bfloat16, "fp32": torch.float32}
+
+
+def _tol(dtype, ref):
+    m = float(np.max(np.abs(ref))) if ref.size else 0.0
+    return 1e-5 * max(1.0, m) if dtype == "fp32" else 2.0 ** -7 * max(m, 1e-2)
+
+
+def _rand(seed, shape, dtype):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn(shape, generator=g).to(TDT[dtype])
+
+
+def _check(name, got, ref, dtype):
+    got = got.cpu().numpy() if isinstance(got, torch.Tensor) else got
+    err, tol = max_abs(got, ref), _tol(dtype, ref)
+    assert err <= tol, f"{name}: max abs err {err:.3g} > {tol:.3g}"
+
+
+def _block_case(seed, B, Sq, Skv, Hq, Hkv, D, dtype, qpos, kvpos):
+    """One block that is the whole key set: out and lse from the oracle's forward."""
+    q, k, v, g = (_rand(seed + i, s, dtype) for i, s in
+                  enumerate(((B, Sq, Hq, D), (B, Skv, Hkv, D), (B, Skv, Hkv, D), (B, Sq, Hq, D))))
+    scale = 1 / math.sqrt(D)
+    qf, kf, vf, gf = (x.float().numpy() for x in (q, k, v, g))
+    out, lse = oracle.attention_rows(qf, kf, vf, qpos, kvpos, scale)
+    ref = oracle.block_bwd(qf, kf, vf, gf, out, lse, qpos, kvpos, scale)
+    d = lambda x: x.to(DEV)  # noqa: E731
+    tq, tk = torch.from_numpy(qpos).to(DEV), torch.from_numpy(kvpos).to(DEV)
+    o_t = torch.from_numpy(out.astype(np.float32)).to(DEV)
+    l_t = torch.from_numpy(lse.astype(np.float32)).to(DEV)
+    delta = cp.attn_bwd_delta(o_t, d(g))
+    dq = torch.full((B, Sq, Hq, D), 7.0, device=DEV)  # overwritten: WRITE flags
+    dk = torch.full((B, Skv, Hkv, D), 7.0, device=DEV)
+    dv = torch.full((B, Skv, Hkv, D), 7.0, device=DEV)
+    cp.block_bwd(d(q), d(k), d(v), d(g), tq, tk, scale, l_t, delta, dq, dk, dv,
+                 cp.BWD_WRITE_DQ | cp.BWD_WRITE_DKV)
+    torch.cuda.synchronize()
+    return (dq, dk, dv), ref, (d(q), d(k), d(v), d(g), tq, tk, scale, l_t, delta)
+
+
+CASES = [
+    # B, Sq, Skv, Hq, Hkv
+    (1, 256, 256, 2, 2),
+    (2, 200, 333, 4, 2),
+    (1, 130, 70, 8, 1),
+    (1, 97, 300, 6, 2),
+    (1, 1, 1, 1, 1),
+    (3, 45, 513, 4, 4),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("case", CASES)
+def test_block_bwd_causal_contiguous(case, dtype):
+    B, Sq, Skv, Hq, Hkv = case
+    qpos = np.arange(Skv - Sq, Skv, dtype=np.int64) if Skv >= Sq else np.arange(Sq, dtype=np.int64)
+    kvpos = np.arange(Skv, dtype=np.int64)
+    got, ref, _ = _block_case(10, B, Sq, Skv, Hq, Hkv, 128, dtype, qpos, kvpos)
+    for name, x, r in zip(("dq", "dk", "dv"), got, ref):
+        _check(name, x, r, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("C,t", [(4, 64), (2, 100)])
+def test_block_bwd_every_zigzag_step_class(C, t, dtype):
+    S = 2 * C * t
+    for r in (0, C - 1):
+        qpos = oracle.zigzag_positions(S, C, r)
+        for o in range(C):
+            kvpos = oracle.zigzag_positions(S, C, o)
+            got, ref, _ = _block_case(20 + o, 1, 2 * t, 2 * t, 4, 2, 128, dtype, qpos, kvpos)
+            for name, x, rr in zip(("dq", "dk", "dv"), got, ref):
+                _check(f"r{r} o{o} {name}", x, rr, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_block_bwd_sparse_positions_and_empty_rows(dtype):
+    rng = np.random.default_rng(4)
+    qpos = np.sort(rng.choice(5000, 150, replace=False)).astype(np.int64)
+    kvpos = np.sort(rng.choice(np.arange(1000, 6000), 260, replace=False)).astype(np.int64)
+    got, ref, _ = _block_case(30, 1, 150, 260, 4, 2, 128, dtype, qpos, kvpos)
+    empty = kvpos[0] > qpos
+    assert empty.any()
+    assert torch.count_nonzero(got[0][:, torch.from_numpy(empty).to(DEV)]) == 0
+    for name, x, r in zip(("dq", "dk", "dv"), got, ref):
+        _check(name, x, r, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_fp32_head_dim_64_and_accumulate_flag(dtype):
+    D = 64 if dtype == "fp32" else 128
+    pos = np.arange(96, dtype=np.int64)
+    got, ref, args = _block_case(40, 1, 96, 96, 2, 1, D, dtype, pos, pos)
+    # a second call without flags adds the same part again: exactly twice the first result
+    first = [x.clone() for x in got]
+    cp.block_bwd(*args, *got, 0)
+    torch.cuda.synchronize()
+    for a, b2 in zip(first, got):
+        assert torch.equal(b2, 2 * a)
+    for name, x, r in zip(("dq", "dk", "dv"), first, ref):
+        _check(name, x, r, dtype)
+
+
+def test_no_keys_with_write_flags_gives_zeros():
+    q = _rand(1, (1, 40, 2, 128), "bf16").to(DEV)
+    k = torch.empty((1, 0, 2, 128), dtype=torch.bfloat16, device=DEV)
+    pos = torch.arange(40, device=DEV)
+    lse = torch.full((1, 2, 40), -math.inf, device=DEV)
+    delta = torch.zeros((1, 2, 40), device=DEV)
+    dq = torch.full((1, 40, 2, 128), 3.0, device=DEV)
+    dk = torch.empty((1, 0, 2, 128), device=DEV)
+    cp.block_bwd(q, k, k, q, pos, pos[:0], 0.1, lse, delta, dq, dk, dk.clone(), cp.BWD_WRITE_DQ)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dq) == 0
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_delta_matches_oracle(dtype):
+    out = _rand(50, (2, 77, 3, 128), "fp32")
+    g = _rand(51, (2, 77, 3, 128), dtype)
+    got = cp.attn_bwd_delta(out.to(DEV), g.to(DEV)).cpu().numpy()
+    ref = np.einsum("bshd,bshd->bhs", out.double().numpy(), g.double().numpy())
+    assert max_abs(got, ref) <= 1e-5 * max(1.0, float(np.abs(ref).max()))
+
+
+def _synthetic_saved(w, qf, kf, zz):
+    """Saved forward state for a full-size check: out is seeded N(0,1) and lse an upper bound
+    of each row's log-sum-exp (scale*|q_i|*max_j|k_j| + ln(visible keys)), so every weight
+    p = exp(s - lse) stays below 1.  The block backward is a function of these inputs whatever
+    their origin, and the oracle evaluates the same function."""
+    B, s, H, D = qf.shape
+    out = torch.randn((B, s, H, D), generator=torch.Generator().manual_seed(77)).numpy()
+    kmax = float(np.sqrt((kf.astype(np.float64) ** 2).sum(-1)).max())
+    qn = np.sqrt((qf.astype(np.float64) ** 2).sum(-1))  # [B, s, H]
+    lse = (w.scale * qn * kmax + np.log(zz + 1.0)[None, :, None]).transpose(0, 2, 1)
+    return out.astype(np.float32), np.ascontiguousarray(lse.astype(np.float32))
+
+
+def _ring_bwd_check(w, rows_per_chunk, key_samples, exact_forward):
+    C, r = w.cp_size, w.rank
+    S = w.seq_len
+    pos = [cp.zigzag_index(S, C, o, device=DEV) for o in range(C)]
+    ks = [gen(w, "k", zigzag_chunks(C, o), w.heads_kv).to(DEV) for o in range(C)]
+    vs = [gen(w, "v", zigzag_chunks(C, o), w.heads_kv).to(DEV) for o in range(C)]
+    q = gen(w, "q", zigzag_chunks(C, r), w.heads_q)
+    g = gen(w, "dout", zigzag_chunks(C, r), w.heads_q)
+    ids = range(2 * C)
+    kf, vf = gen(w, "k", ids, w.heads_kv).float().numpy(), gen(w, "v", ids, w.heads_kv).float().numpy()
+    zz = oracle.zigzag_positions(S, C, r)
+    gpos = np.arange(S, dtype=np.int64)
+    qf, gf = q.float().numpy(), g.float().numpy()
+    if exact_forward:  # the complete forward of every local row, from the oracle
+        out, lse = oracle.attention_rows(qf, kf, vf, zz, gpos, w.scale)
+    else:
+        out, lse = _synthetic_saved(w, qf, kf, zz)
+    print(f"{w.name}: saved forward state ready", flush=True)
+    o_t = torch.from_numpy(np.ascontiguousarray(out, dtype=np.float32)).to(DEV)
+    l_t = torch.from_numpy(np.ascontiguousarray(lse, dtype=np.float32)).to(DEV)
+    dq, dks, dvs = cp.ring_share_bwd(q.to(DEV), ks, vs, pos, r, w.scale, o_t, l_t, g.to(DEV))
+    torch.cuda.synchronize()
+    print(f"{w.name}: HIP ring backward done", flush=True)
+    del ks, vs
+    qrows = sample_rows(w.local_len, w.chunk_len, seed=r, per_chunk_random=rows_per_chunk)
+    ref_dq, _, _ = oracle.block_bwd(qf, kf, vf, gf, out, lse, zz, gpos, w.scale, qrows=qrows,
+                                    krows=np.zeros(0, dtype=np.int64))
+    _check("dq", dq[:, torch.from_numpy(qrows).to(DEV)], ref_dq, w.dtype)
+    print(f"{w.name}: dq checked on {len(qrows)} rows", flush=True)
+    rng = np.random.default_rng(9)
+    for o in range(C):
+        kz = oracle.zigzag_positions(S, C, o)
+        krows = np.unique(np.concatenate([[0, w.chunk_len - 1, w.chunk_len, 2 * w.chunk_len - 1],
+                                          rng.integers(0, 2 * w.chunk_len, key_samples)])).astype(np.int64)
+        _, rdk, rdv = oracle.block_bwd(qf, kf[:, kz], vf[:, kz], gf, out, lse, zz, kz, w.scale,
+                                       qrows=np.zeros(0, dtype=np.int64), krows=krows)
+        kidx = torch.from_numpy(krows).to(DEV)
+        _check(f"dk owner {o}", dks[o][:, kidx], rdk, w.dtype)
+        _check(f"dv owner {o}", dvs[o][:, kidx], rdv, w.dtype)
+        print(f"{w.name}: owner {o} dk, dv checked on {len(krows)} keys", flush=True)
+
+
+def test_ring_share_bwd_8k():
+    _ring_bwd_check(WORKLOADS["rank_share_8k"], rows_per_chunk=12, key_samples=12, exact_forward=True)
+
+
+def test_ring_share_bwd_256k_sampled():
+    _ring_bwd_check(WORKLOADS["ring_share_256k"], rows_per_chunk=2, key_samples=4, exact_forward=False)
