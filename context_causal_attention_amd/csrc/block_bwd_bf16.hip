@@ -115,6 +115,19 @@ __device__ inline f32x16 mfma(const bf16x8& a, const bf16x8& b, const f32x16& c)
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Scheduling hint for a loop of N steps, each of M matrix-core products fed by R LDS reads:
+// issue the reads A steps ahead of the products that use them (sync group G).
+template <int N, int M, int R, int G, int A = 2>
+__device__ inline void sched_reads_ahead() {
+    __builtin_amdgcn_sched_group_barrier(0x100, R * A, G);
+#pragma unroll
+    for (int i = 0; i < N - A; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, M, G);
+        __builtin_amdgcn_sched_group_barrier(0x100, R, G);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, M * A, G);
+}
+
 // Tiles in LDS are row-major (256 bytes per row) with 16-byte chunk c of row r stored at
 // chunk c ^ (r & 15): row reads of 16 consecutive rows are conflict-free, and transposed reads
 // of 4 rows by 16-lane groups stay within two passes.
@@ -291,6 +304,7 @@ __global__ void __launch_bounds__(kThreads, 1) block_bwd_dq_kernel(const BwdPara
                 s[kb] = mfma(ka, qreg[ks], s[kb]);
                 dp[kb] = mfma(va, doreg[ks], dp[kb]);
             }
+        sched_reads_ahead<16, 2, 2, 1>();
 
         // ds = p (dp - D); entry v of key block kb is key 32*kb + 8*(v/4) + 4*half + v%4
         const bool masked = jt >= n_full;
@@ -317,6 +331,7 @@ __global__ void __launch_bounds__(kThreads, 1) block_bwd_dq_kernel(const BwdPara
                     const bf16x8 a = lds_tr_pair(base + off_t[db].a, base + off_t[db].b);
                     acc[db] = mfma(a, dsb[kb][ks2], acc[db]);
                 }
+        sched_reads_ahead<16, 1, 2, 2>();
 
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next tile has landed
         __syncthreads();
@@ -521,6 +536,7 @@ __global__ void __launch_bounds__(kThreads, 1) block_bwd_dkdv_kernel(const BwdPa
                 s = mfma(qa, kreg[ks], s);
                 dp = mfma(ga, vreg[ks], dp);
             }
+            sched_reads_ahead<8, 2, 2, 3>();
             // entry v is query row qb*32 + 8*(v/4) + 4*half + v%4 of the tile, key l32
             const int64_t rel = first - qt * kTile - qb * 32 - 4 * half;
             const int lim = rel < 0 ? 0 : (rel > 32 ? 32 : (int)rel);
@@ -550,6 +566,7 @@ __global__ void __launch_bounds__(kThreads, 1) block_bwd_dkdv_kernel(const BwdPa
                     dv[db] = mfma(ga, pb[ks2], dv[db]);
                     dk[db] = mfma(qa, dsb[ks2], dk[db]);
                 }
+            sched_reads_ahead<8, 2, 4, 4>();
         }
         // every wave is done with this stage; the next one (tiles and row values) is in place
         if (u + 1 < n_steps) store_rowvals(nxt, nextv);
