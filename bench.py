@@ -49,8 +49,9 @@ def parse_args(argv=None):
     ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
                     help="bwd: time the ring-share backward (delta + one block backward per ring "
                          "step) instead of the forward; ring_share workloads only")
-    ap.add_argument("--unfused", action="store_true",
-                    help="ring share: write each step's tile and merge it with the separate merge kernel")
+    ap.add_argument("--mode", choices=("single", "fused", "unfused"), default="single",
+                    help="ring share: one launch over all ring blocks (single), one launch per step "
+                         "merging in its epilogue (fused), or per-step tiles plus the merge kernel")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -62,7 +63,7 @@ def parse_args(argv=None):
 class Plan:
     """Buffers and the launch sequence of one step of a workload."""
 
-    def __init__(self, w, dev, fused=True, backward=False):
+    def __init__(self, w, dev, mode="single", backward=False):
         import torch
         import context_causal_attention_amd as cp
         from context_causal_attention_amd import synthetic
@@ -72,7 +73,7 @@ class Plan:
         kw = dict(batch=w.batch, chunk_len=w.chunk_len, head_dim=w.head_dim, dtype=td)
         C = w.cp_size
         self.kind = w.kind
-        self.fused = fused
+        self.mode = mode
         self.attn_flops = []   # FLOPs of each block attention launch of a step, in order
         if w.kind == "ring_share":
             # the rank's share, or every rank's share when the workload names no rank
@@ -83,7 +84,7 @@ class Plan:
             self.pos = [torch.empty(w.local_len, dtype=torch.int64, device=dev) for _ in range(C)]
             self.out = torch.empty((w.batch, w.local_len, w.heads_q, w.head_dim), dtype=torch.float32, device=dev)
             self.lse = torch.empty((w.batch, w.heads_q, w.local_len), dtype=torch.float32, device=dev)
-            if not fused:
+            if mode == "unfused":
                 self.tout = torch.empty_like(self.out)
                 self.tlse = torch.empty_like(self.lse)
             t = w.chunk_len
@@ -204,12 +205,16 @@ class Plan:
                 cp.zigzag_index(w.seq_len, C, o, out=self.pos[o])
             for r in self.ranks:
                 q = self.qs[r]
-                for step in range(C):
-                    owner = (r - step) % C
+                order = [(r - step) % C for step in range(C)]
+                if self.mode == "single":
+                    attn(q, [self.k[o] for o in order], [self.v[o] for o in order], [self.pos[o] for o in order],
+                         self.pos[r], w.scale, self.out, self.lse, fn=cp.ring_blocks_fwd)
+                    continue
+                for step, owner in enumerate(order):
                     a = (q, self.k[owner], self.v[owner], self.pos[r], self.pos[owner], w.scale)
                     if step == 0:
                         attn(*a, self.out, self.lse)
-                    elif self.fused:
+                    elif self.mode == "fused":
                         attn(*a, self.out, self.lse, fn=cp.block_fwd_merge)
                     else:
                         attn(*a, self.tout, self.tlse)
@@ -363,7 +368,7 @@ def main(argv=None) -> int:
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    plan = Plan(w, dev, fused=not args.unfused, backward=args.which == "bwd")
+    plan = Plan(w, dev, mode=args.mode, backward=args.which == "bwd")
     if args.copy_calibration_mib > 0:
         import context_causal_attention_amd as cp
         n = args.copy_calibration_mib << 20
@@ -405,7 +410,7 @@ def main(argv=None) -> int:
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic (seeded iid N(0,1), per-chunk generators)",
-        "config": {"workload": w.name + ("_unfused" if args.unfused and w.kind == "ring_share" else "")
+        "config": {"workload": w.name + (f"_{args.mode}" if args.mode != "single" and w.kind == "ring_share" else "")
                    + ("_bwd" if bwd else ""),
                    "batch": w.batch, "a2a": w.a2a, "zigzag": w.zigzag, "seq_len": w.seq_len, "cp_size": w.cp_size,
                    "rank": w.rank, "group": w.group, "heads_q": w.heads_q, "heads_kv": w.heads_kv,

@@ -22,6 +22,7 @@ from ._binding import (  # noqa: F401
     load_library,
     lse_merge,
     reorder_gathered,
+    ring_blocks_fwd,
     ring_share_bwd,
     ring_share_fwd,
     ulysses_heads_to_seq,

@@ -56,6 +56,7 @@ def load_library():
     L.cpattn_block_fwd.argtypes = [P, P, P, ctypes.c_int, i32, i64, i64, i32, i32, i32, P, P, f32, P, P, P]
     L.cpattn_block_fwd_merge.argtypes = list(L.cpattn_block_fwd.argtypes)
     L.cpattn_lse_merge.argtypes = [P, P, P, P, i32, i64, i32, i32, P]
+    L.cpattn_ring_share_fwd.argtypes = [P, P, P, P, P, i32, ctypes.c_int, i32, i64, i32, i32, i32, P, f32, P, P, P]
     L.cpattn_attn_bwd_delta.argtypes = [P, P, ctypes.c_int, i32, i64, i32, i32, P, P]
     L.cpattn_block_bwd.argtypes = [P, P, P, P, ctypes.c_int, i32, i64, i64, i32, i32, i32, P, P, f32, P, P, P,
                                    P, P, ctypes.c_uint32, P]
@@ -63,7 +64,7 @@ def load_library():
     L.cpattn_ulysses_permute.argtypes = [P, P, i32, i32, i64, i32, i32, i32, i32, ctypes.c_int, P]
     L.cpattn_ulysses_permute_zigzag.argtypes = list(L.cpattn_ulysses_permute.argtypes)
     for name in ("cpattn_zigzag_index", "cpattn_block_fwd", "cpattn_block_fwd_merge", "cpattn_lse_merge",
-                 "cpattn_attn_bwd_delta", "cpattn_block_bwd",
+                 "cpattn_attn_bwd_delta", "cpattn_block_bwd", "cpattn_ring_share_fwd",
                  "cpattn_reorder_gathered", "cpattn_ulysses_permute", "cpattn_ulysses_permute_zigzag"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
@@ -219,37 +220,76 @@ def ulysses_heads_to_seq(grouped: torch.Tensor, group: int, out: torch.Tensor,
     return out
 
 
+def ring_blocks_fwd(q: torch.Tensor, k_blocks, v_blocks, kv_positions, q_pos: torch.Tensor, scale: float,
+                    out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    """One launch over K/V blocks taken in the given order (cpattn_ring_share_fwd):
+    q [B, Sq, Hq, D]; k_blocks[o], v_blocks[o] [B, S_o, Hkv, D]; kv_positions[o] [S_o]."""
+    L = load_library()
+    n = len(k_blocks)
+    if not (len(v_blocks) == len(kv_positions) == n):
+        raise ValueError("k_blocks, v_blocks and kv_positions must have the same length")
+    B, Sq, Hq, D = q.shape
+    _need(q, "q")
+    _need(q_pos, "q_pos", torch.int64, (Sq,))
+    Hkv = k_blocks[0].shape[2]
+    for o in range(n):
+        So = k_blocks[o].shape[1]
+        _need(k_blocks[o], f"k_blocks[{o}]", q.dtype, (B, So, Hkv, D))
+        _need(v_blocks[o], f"v_blocks[{o}]", q.dtype, (B, So, Hkv, D))
+        _need(kv_positions[o], f"kv_positions[{o}]", torch.int64, (So,))
+    if out is None:
+        out = torch.empty((B, Sq, Hq, D), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, (B, Sq, Hq, D))
+    _need(lse, "lse", torch.float32, (B, Hq, Sq))
+    kp = (ctypes.c_void_p * n)(*[t.data_ptr() for t in k_blocks])
+    vp = (ctypes.c_void_p * n)(*[t.data_ptr() for t in v_blocks])
+    pp = (ctypes.c_void_p * n)(*[t.data_ptr() for t in kv_positions])
+    sq = (ctypes.c_int64 * n)(*[t.shape[1] for t in k_blocks])
+    dt = CPATTN_BF16 if q.dtype == torch.bfloat16 else CPATTN_F32
+    _check(L.cpattn_ring_share_fwd(_ptr(q), kp, vp, pp, sq, n, dt, B, Sq, Hq, Hkv, D, _ptr(q_pos), float(scale),
+                                   _ptr(out), _ptr(lse), _stream(q.device)))
+    return out, lse
+
+
 def ring_share_fwd(q: torch.Tensor, k_blocks, v_blocks, positions, rank: int, scale: float,
                    out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
                    tile_out: torch.Tensor | None = None, tile_lse: torch.Tensor | None = None,
-                   fused: bool = True):
-    """Rank ``rank``'s share over the C ring steps, back to back on the current stream.
+                   mode: str = "single"):
+    """Rank ``rank``'s share over the C ring steps, on the current stream.
 
     Step i attends the K/V block of owner (rank - i) mod C ("On Context Parallelism",
     Peer-to-peer / Forward): ``k_blocks[o]``, ``v_blocks[o]`` and ``positions[o]`` are owner
     o's shard and its global positions; ``positions[rank]`` are also the query positions.
-    Step 0 writes the accumulator directly.  With ``fused`` each later step merges its block
-    into the accumulator inside the attention launch (``block_fwd_merge``); otherwise it
-    writes a tile (``tile_out``, ``tile_lse``) and folds it in with ``lse_merge``.  Both give
-    the same bits.  Returns (out, lse).
-    """
+    ``mode``:
+      "single"  one launch over all C blocks in ring order (one running softmax);
+      "fused"   one launch per step, steps >= 1 merged into (out, lse) in the epilogue;
+      "unfused" one launch per step into a tile (``tile_out``, ``tile_lse``), then the merge
+                kernel.  "fused" and "unfused" give the same bits.
+    Returns (out, lse)."""
     C = len(k_blocks)
     B, s, Hq, D = q.shape
+    order = [(rank - step) % C for step in range(C)]
+    if mode == "single":
+        return ring_blocks_fwd(q, [k_blocks[o] for o in order], [v_blocks[o] for o in order],
+                               [positions[o] for o in order], positions[rank], scale, out, lse)
+    if mode not in ("fused", "unfused"):
+        raise ValueError(f"unknown mode {mode!r}")
     if out is None:
         out = torch.empty((B, s, Hq, D), dtype=torch.float32, device=q.device)
     if lse is None:
         lse = torch.empty((B, Hq, s), dtype=torch.float32, device=q.device)
-    if C > 1 and not fused:
+    if C > 1 and mode == "unfused":
         if tile_out is None:
             tile_out = torch.empty_like(out)
         if tile_lse is None:
             tile_lse = torch.empty_like(lse)
-    for step in range(C):
-        owner = (rank - step) % C
+    for step, owner in enumerate(order):
         args = (q, k_blocks[owner], v_blocks[owner], positions[rank], positions[owner], scale)
         if step == 0:
             block_fwd(*args, out, lse)
-        elif fused:
+        elif mode == "fused":
             block_fwd_merge(*args, out, lse)
         else:
             block_fwd(*args, tile_out, tile_lse)

@@ -108,6 +108,8 @@ cpattn_status_t block_fwd_common(const char* name, bool merge, const void* q, co
         return fail(CPATTN_ERR_UNSUPPORTED, "%s: launch grid too large", name);
     cpattn::BlockFwdArgs a{q,     k,      v,       q_positions, kv_positions, out,      lse,
                            batch, seq_q, seq_kv, heads_q,     heads_kv,     head_dim, scale, merge};
+    a.n_blk = 1;
+    a.blk[0] = cpattn::KVBlockArg{k, v, kv_positions, seq_kv};
     if (seq_kv == 0) {
         // no keys at all: every row is empty (out = 0, lse = -inf)
         return from_hip(cpattn::launch_block_fwd_empty(a, (hipStream_t)stream), name);
@@ -213,6 +215,67 @@ CPATTN_API cpattn_status_t cpattn_block_bwd(const void* q, const void* k, const 
     const hipError_t e = (dtype == CPATTN_BF16) ? cpattn::launch_block_bwd_bf16(a, (hipStream_t)stream)
                                                 : cpattn::launch_block_bwd_f32(a, (hipStream_t)stream);
     return from_hip(e, name);
+}
+
+CPATTN_API cpattn_status_t cpattn_ring_share_fwd(const void* q, const void* const* k_blocks,
+                                                 const void* const* v_blocks,
+                                                 const int64_t* const* kv_positions, const int64_t* seq_kv,
+                                                 int32_t n_blocks, cpattn_dtype_t dtype, int32_t batch,
+                                                 int64_t seq_q, int32_t heads_q, int32_t heads_kv,
+                                                 int32_t head_dim, const int64_t* q_positions, float scale,
+                                                 float* out, float* lse, void* stream) {
+    const char* name = "ring_share_fwd";
+    if (n_blocks <= 0 || n_blocks > cpattn::kMaxRingBlocks)
+        return fail(CPATTN_ERR_INVALID_ARG, "%s: n_blocks %d outside [1, %d]", name, n_blocks,
+                    cpattn::kMaxRingBlocks);
+    if (!k_blocks || !v_blocks || !kv_positions || !seq_kv)
+        return fail(CPATTN_ERR_INVALID_ARG, "%s: NULL block array", name);
+    for (int32_t o = 0; o < n_blocks; ++o)
+        if (seq_kv[o] < 0) return fail(CPATTN_ERR_INVALID_ARG, "%s: seq_kv[%d] < 0", name, o);
+    if (dtype != CPATTN_BF16) {
+        // fp32: one block at a time, the later ones merged in the epilogue
+        for (int32_t o = 0; o < n_blocks; ++o) {
+            const cpattn_status_t st =
+                block_fwd_common(name, o > 0, q, k_blocks[o], v_blocks[o],
+                                 dtype, batch, seq_q, seq_kv[o], heads_q, heads_kv, head_dim, q_positions,
+                                 kv_positions[o], scale, out, lse, stream);
+            if (st != CPATTN_OK) return st;
+        }
+        return ok();
+    }
+    // validate every block as a single-block call would, without launching
+    for (int32_t o = 0; o < n_blocks; ++o) {
+        if (seq_kv[o] > 0 && (!k_blocks[o] || !v_blocks[o] || !kv_positions[o]))
+            return fail(CPATTN_ERR_INVALID_ARG, "%s: block %d has a NULL pointer", name, o);
+        if (seq_kv[o] > 0 && (!aligned16(k_blocks[o]) || !aligned16(v_blocks[o])))
+            return fail(CPATTN_ERR_UNSUPPORTED, "%s: block %d not 16-byte aligned", name, o);
+    }
+    if (batch <= 0 || heads_q <= 0 || heads_kv <= 0)
+        return fail(CPATTN_ERR_INVALID_ARG, "%s: batch and head counts must be > 0", name);
+    if (seq_q < 0) return fail(CPATTN_ERR_INVALID_ARG, "%s: seq_q must be >= 0", name);
+    if (!(scale > 0.f) || !isfinite(scale))
+        return fail(CPATTN_ERR_INVALID_ARG, "%s: scale must be finite and > 0", name);
+    if (heads_q % heads_kv != 0)
+        return fail(CPATTN_ERR_SHAPE, "%s: heads_q %d not a multiple of heads_kv %d", name, heads_q, heads_kv);
+    if (head_dim != 128) return fail(CPATTN_ERR_UNSUPPORTED, "%s: bf16 path supports head_dim 128 only", name);
+    if (seq_q == 0) return ok();
+    if (!q || !q_positions || !out || !lse)
+        return fail(CPATTN_ERR_INVALID_ARG, "%s: q, q_positions, out and lse must be non-NULL", name);
+    if (!aligned16(q) || !aligned16(out))
+        return fail(CPATTN_ERR_UNSUPPORTED, "%s: bf16 path needs 16-byte aligned q and out", name);
+    if ((seq_q + 31) / 32 * (int64_t)batch * heads_kv > kMaxGrid)
+        return fail(CPATTN_ERR_UNSUPPORTED, "%s: launch grid too large", name);
+    cpattn::BlockFwdArgs a{q, nullptr, nullptr, q_positions, nullptr, out,      lse,   batch,
+                           seq_q, 0,   heads_q, heads_kv,    head_dim, scale,   false};
+    a.n_blk = 0;
+    for (int32_t o = 0; o < n_blocks; ++o) {
+        if (seq_kv[o] == 0) continue;  // no keys: contributes nothing
+        a.blk[a.n_blk++] = cpattn::KVBlockArg{k_blocks[o], v_blocks[o], kv_positions[o], seq_kv[o]};
+    }
+    if (a.n_blk == 0) return from_hip(cpattn::launch_block_fwd_empty(a, (hipStream_t)stream), name);
+    a.k = a.blk[0].k;
+    a.seq_kv = a.blk[0].seq;
+    return from_hip(cpattn::launch_block_fwd_bf16(a, (hipStream_t)stream), name);
 }
 
 CPATTN_API cpattn_status_t cpattn_lse_merge(float* out, float* lse, const float* out_tile,

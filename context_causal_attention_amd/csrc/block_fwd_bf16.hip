@@ -64,17 +64,22 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.0f;       // raise the running max only past this margin (log2)
 constexpr float kLazyWeight = 256.0f;  // 2^kLazy
+constexpr int kMaxBlocks = kMaxRingBlocks;  // K/V blocks of one launch
+
+// One K/V block: keys [B][seq][heads_kv][D] and their positions.
+struct KVBlock {
+    const __bf16* k;
+    const __bf16* v;
+    const int64_t* pos;
+    int64_t seq;
+};
 
 struct Params {
     const __bf16* q;
-    const __bf16* k;
-    const __bf16* v;
     const int64_t* qpos;
-    const int64_t* kvpos;
     float* out;
     float* lse;
     int64_t seq_q;
-    int64_t seq_kv;
     int64_t n_qt;      // query tiles of PQ positions
     int32_t heads_q;
     int32_t heads_kv;
@@ -86,6 +91,8 @@ struct Params {
     int32_t xcd_cols;  // n_cols / 8 when n_cols % 8 == 0, else 0
     float c;           // scale * log2(e)
     int32_t merge;     // merge into (out, lse) instead of overwriting them
+    int32_t n_blk;     // K/V blocks attended in turn, as one softmax over all their keys
+    KVBlock blk[kMaxBlocks];
 };
 
 __device__ inline int wave_sum(int x) {
@@ -167,36 +174,52 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
     const int64_t pmin = p.qpos[q0];
     const int64_t pmax = p.qpos[q_last];
 
-    // ---- visible tiles (a prefix) and tiles visible to every query of the block
-    const int64_t n_tiles = (p.seq_kv + kBN - 1) / kBN;
-    int c_ne = 0, c_full = 0;
-    for (int64_t t = tid; t < n_tiles; t += kThreads) {
-        c_ne += (p.kvpos[t * kBN] <= pmax) ? 1 : 0;
-        const int64_t lk = t * kBN + kBN - 1;
-        c_full += (lk < p.seq_kv && p.kvpos[lk] <= pmin) ? 1 : 0;
+    // ---- per K/V block: visible tiles (a prefix) and tiles visible to every query of this
+    // workgroup; then the tile sequence runs over the blocks in turn
+    __shared__ int blk_ne[kMaxBlocks], blk_full[kMaxBlocks];
+    for (int o = 0; o < p.n_blk; ++o) {
+        const int64_t* kp = p.blk[o].pos;
+        const int64_t seq_o = p.blk[o].seq;
+        const int64_t n_tiles = (seq_o + kBN - 1) / kBN;
+        int c_ne = 0, c_full = 0;
+        for (int64_t t = tid; t < n_tiles; t += kThreads) {
+            c_ne += (kp[t * kBN] <= pmax) ? 1 : 0;
+            const int64_t lk = t * kBN + kBN - 1;
+            c_full += (lk < seq_o && kp[lk] <= pmin) ? 1 : 0;
+        }
+        c_ne = wave_sum(c_ne);
+        c_full = wave_sum(c_full);
+        if (lane == 0) {
+            red[w] = c_ne;
+            red[NW + w] = c_full;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            int a = 0, f = 0;
+            for (int i = 0; i < NW; ++i) {
+                a += red[i];
+                f += red[NW + i];
+            }
+            blk_ne[o] = a;
+            blk_full[o] = f;
+        }
+        __syncthreads();
     }
-    c_ne = wave_sum(c_ne);
-    c_full = wave_sum(c_full);
-    if (lane == 0) {
-        red[w] = c_ne;
-        red[NW + w] = c_full;
-    }
-    __syncthreads();
-    int n_ne = 0, n_full = 0;
-#pragma unroll
-    for (int i = 0; i < NW; ++i) {
-        n_ne += red[i];
-        n_full += red[NW + i];
-    }
+    int n_total = 0;  // tiles over all blocks
+    for (int o = 0; o < p.n_blk; ++o) n_total += blk_ne[o];
 
     // ---- K/V tile loads: each wave fills (64 / NW) rows of K and of V per tile, four rows
     // (1 KB) per instruction; lane -> row (lane >> 4), stored chunk (lane & 15).  The source
     // address is a wave-uniform tile base plus a per-lane byte offset fixed for the kernel;
     // only a ragged last tile clamps its rows (to the last key, finite data the mask hides).
     const int64_t kvstride = (int64_t)p.heads_kv * kD;  // elements between consecutive keys
-    const char* kbase = (const char*)(p.k + (b * p.seq_kv * p.heads_kv + kvh) * (int64_t)kD);
-    const char* vbase = (const char*)(p.v + (b * p.seq_kv * p.heads_kv + kvh) * (int64_t)kD);
     const int64_t tile_bytes_g = (int64_t)kBN * kvstride * 2;  // global bytes between tiles
+    auto kbase_of = [&](int o) {
+        return (const char*)(p.blk[o].k + (b * p.blk[o].seq * p.heads_kv + kvh) * (int64_t)kD);
+    };
+    auto vbase_of = [&](int o) {
+        return (const char*)(p.blk[o].v + (b * p.blk[o].seq * p.heads_kv + kvh) * (int64_t)kD);
+    };
     constexpr int kRowsPerWave = kBN / NW;
     constexpr int kLoadsPerWave = kRowsPerWave / 4;
     const int ld_row_in = lane >> 4;   // row within the 4-row slab
@@ -208,11 +231,13 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
         koff[i] = (uint32_t)(row * kvstride * 2) + ((ld_chunk ^ (row & 15)) << 4);
         voff[i] = (uint32_t)(row * kvstride * 2) + ((ld_chunk ^ ((row & 3) << 2)) << 4);
     }
-    auto issue_tile = [&](int jt, LDS_AS char* kt) {
+    // tile jt of block o into the stage at kt
+    auto issue_tile = [&](int o, int jt, LDS_AS char* kt) {
         LDS_AS char* vt = kt + kTileBytes;
-        const char* kb_t = kbase + (int64_t)jt * tile_bytes_g;
-        const char* vb_t = vbase + (int64_t)jt * tile_bytes_g;
-        if ((int64_t)(jt + 1) * kBN <= p.seq_kv) {
+        const char* kb_t = kbase_of(o) + (int64_t)jt * tile_bytes_g;
+        const char* vb_t = vbase_of(o) + (int64_t)jt * tile_bytes_g;
+        const int64_t seq_o = p.blk[o].seq;
+        if ((int64_t)(jt + 1) * kBN <= seq_o) {
 #pragma unroll
             for (int i = 0; i < kLoadsPerWave; ++i) {
                 load_lds16(kb_t + koff[i], kt + (w * kRowsPerWave + 4 * i) * kRowBytes);
@@ -223,7 +248,7 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
             for (int i = 0; i < kLoadsPerWave; ++i) {
                 const int row = w * kRowsPerWave + 4 * i + ld_row_in;
                 const int64_t j = (int64_t)jt * kBN + row;
-                const int64_t over = (j >= p.seq_kv) ? (j - (p.seq_kv - 1)) * kvstride * 2 : 0;
+                const int64_t over = (j >= seq_o) ? (j - (seq_o - 1)) * kvstride * 2 : 0;
                 load_lds16(kb_t + koff[i] - over, kt + (w * kRowsPerWave + 4 * i) * kRowBytes);
                 load_lds16(vb_t + voff[i] - over, vt + (w * kRowsPerWave + 4 * i) * kRowBytes);
             }
@@ -253,24 +278,28 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
         }
     }
 
-    // number of keys visible to each of this lane's query rows, needed only when some tile
-    // is partly visible: positions increase, so it is found by binary search within the
-    // keys of the partly visible tiles [n_full*kBN, min(n_ne*kBN, seq_kv))
+    // number of keys of block o visible to each of this lane's query rows, needed only when
+    // some tile of o is partly visible: positions increase, so it is found by binary search
+    // within the keys of the partly visible tiles [n_full*kBN, min(n_ne*kBN, seq))
     int64_t vis[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) vis[nb] = 0;
-    if (n_full < n_ne) {
+    auto find_vis = [&](int o) {
+        const int ne = blk_ne[o], full = blk_full[o];
+        const int64_t seq_o = p.blk[o].seq;
+        const int64_t* kp = p.blk[o].pos;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            int64_t lo = (int64_t)n_full * kBN;
-            int64_t hi = (int64_t)n_ne * kBN < p.seq_kv ? (int64_t)n_ne * kBN : p.seq_kv;
-            while (lo < hi) {
-                const int64_t mid = (lo + hi) >> 1;
-                if (p.kvpos[mid] <= mypos[nb]) lo = mid + 1; else hi = mid;
+            vis[nb] = 0;
+            if (full < ne) {
+                int64_t lo = (int64_t)full * kBN;
+                int64_t hi = (int64_t)ne * kBN < seq_o ? (int64_t)ne * kBN : seq_o;
+                while (lo < hi) {
+                    const int64_t mid = (lo + hi) >> 1;
+                    if (kp[mid] <= mypos[nb]) lo = mid + 1; else hi = mid;
+                }
+                vis[nb] = lo;
             }
-            vis[nb] = lo;
         }
-    }
+    };
 
     f32x16 acc_o[NB][kD / 32];
     float m_run[NB], l_run[NB];
@@ -303,10 +332,20 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
     LDS_AS char* st0 = (LDS_AS char*)lds_stage0;
     LDS_AS char* st1 = (LDS_AS char*)lds_stage1;
 
-    // one tile: prefetch tile jt+1 into `nxt`, compute tile jt from `cur`
-    auto tile = [&](int jt, const LDS_AS char* kt, LDS_AS char* nxt) {
+    // cursors: the tile being computed (block oc, tile jt; n_full of oc) and the next one to
+    // load (block on, tile jn; on == p.n_blk when there is none)
+    int oc = 0, jt = 0, n_full = 0;
+    int on = 0, jn = 0;
+    auto advance = [&](int& o, int& j) {
+        if (++j >= blk_ne[o]) {
+            j = 0;
+            do { ++o; } while (o < p.n_blk && blk_ne[o] == 0);
+        }
+    };
+    // one tile: prefetch the next tile into `nxt`, compute the current one from `cur`
+    auto tile = [&](const LDS_AS char* kt, LDS_AS char* nxt) {
         const LDS_AS char* vt = kt + kTileBytes;
-        if (jt + 1 < n_ne) issue_tile(jt + 1, nxt);
+        if (on < p.n_blk) issue_tile(on, jn, nxt);
 
         // S^T = K Q^T
         f32x16 s[NB][2];
@@ -424,14 +463,29 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
         // the next tile has landed in LDS (own loads) and every wave is done with this one
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), visible to the compiler
         __syncthreads();
+        const int o_prev = oc;
+        advance(oc, jt);
+        if (on < p.n_blk) advance(on, jn);
+        if (oc != o_prev && oc < p.n_blk) {
+            n_full = blk_full[oc];
+            find_vis(oc);
+        }
     };
 
-    if (n_ne > 0) issue_tile(0, st0);
+    while (oc < p.n_blk && blk_ne[oc] == 0) ++oc;  // first block with a visible tile
+    if (oc < p.n_blk) {
+        n_full = blk_full[oc];
+        find_vis(oc);
+        issue_tile(oc, 0, st0);
+        on = oc;
+        jn = 0;
+        advance(on, jn);
+    }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), visible to the compiler
     __syncthreads();
-    for (int jt = 0; jt < n_ne; jt += 2) {
-        tile(jt, st0, st1);
-        if (jt + 1 < n_ne) tile(jt + 1, st1, st0);
+    for (int u = 0; u < n_total; u += 2) {
+        tile(st0, st1);
+        if (u + 1 < n_total) tile(st1, st0);
     }
 
     // ---- epilogue: combine the half-wave row sums, normalise, store (or merge into out, lse)
@@ -492,14 +546,13 @@ hipError_t launch_variant(Params p, int64_t seq_q, hipStream_t stream) {
 hipError_t launch_block_fwd_bf16(const BlockFwdArgs& a, hipStream_t stream) {
     Params p;
     p.q = (const __bf16*)a.q;
-    p.k = (const __bf16*)a.k;
-    p.v = (const __bf16*)a.v;
     p.qpos = a.q_pos;
-    p.kvpos = a.kv_pos;
     p.out = a.out;
     p.lse = a.lse;
     p.seq_q = a.seq_q;
-    p.seq_kv = a.seq_kv;
+    p.n_blk = a.n_blk;
+    for (int o = 0; o < a.n_blk; ++o)
+        p.blk[o] = KVBlock{(const __bf16*)a.blk[o].k, (const __bf16*)a.blk[o].v, a.blk[o].pos, a.blk[o].seq};
     p.heads_q = a.heads_q;
     p.heads_kv = a.heads_kv;
     p.ratio = a.heads_q / a.heads_kv;

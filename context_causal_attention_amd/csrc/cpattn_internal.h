@@ -24,6 +24,15 @@ hipError_t launch_ulysses_permute(const void* in, void* out, int32_t elem_bytes,
                                   int32_t cp_size, int32_t group, int32_t dir, bool zigzag,
                                   hipStream_t stream);
 
+constexpr int kMaxRingBlocks = 16;  // K/V blocks one ring-share launch can take
+
+struct KVBlockArg {
+    const void* k;
+    const void* v;
+    const int64_t* pos;
+    int64_t seq;
+};
+
 struct BlockFwdArgs {
     const void* q;
     const void* k;
@@ -42,6 +51,10 @@ struct BlockFwdArgs {
     // false: write the block's (out, lse).  true: (out, lse) hold an accumulator and the
     // block's result is merged into it in the epilogue, with the arithmetic of merge_math.h.
     bool merge;
+    // bf16 path: the K/V blocks attended in turn (one softmax over all their keys); a single
+    // block call fills blk[0] from k, v, kv_pos, seq_kv
+    int32_t n_blk;
+    KVBlockArg blk[kMaxRingBlocks];
 };
 
 // No keys: writes out = 0 and lse = -inf for every row (merge: merges that empty result).

@@ -151,6 +151,34 @@ cpattn_status_t cpattn_block_fwd_merge(const void* q, const void* k, const void*
                                        float* lse, void* stream);
 
 /*
+ * cpattn_ring_share_fwd -- a rank's whole share in one launch: the queries against C K/V
+ * blocks taken in the given (ring) order, as [CP] "Peer-to-peer" / "Forward" computes them
+ * step by step with the merge of attention tiles.  Here each workgroup walks the blocks'
+ * visible tiles one after another with a single running softmax, so the per-step results
+ * are never formed: the output is the merge of the C block results (equal in exact
+ * arithmetic; rounded once instead of C times).  This is the persistent launch over all
+ * ring blocks; on one GPU it removes the per-step launches, their tails and the merges.
+ *
+ *   q, q_positions, scale, out, lse   as for cpattn_block_fwd (out, lse are written)
+ *   k_blocks, v_blocks   host arrays of n_blocks DEVICE pointers, block o of shape
+ *                        [batch][seq_kv[o]][heads_kv][head_dim], dtype
+ *   kv_positions         host array of n_blocks DEVICE pointers to int64 [seq_kv[o]],
+ *                        each strictly increasing
+ *   seq_kv               host array of n_blocks lengths (0: the block is skipped)
+ *   n_blocks             1 .. 16
+ * dtype CPATTN_BF16: one launch (head_dim 128).  CPATTN_F32: cpattn_block_fwd on the first
+ * block and cpattn_block_fwd_merge on the others.
+ * Errors: as for cpattn_block_fwd, and INVALID_ARG for n_blocks outside [1, 16] or NULL
+ * arrays.
+ */
+cpattn_status_t cpattn_ring_share_fwd(const void* q, const void* const* k_blocks,
+                                      const void* const* v_blocks, const int64_t* const* kv_positions,
+                                      const int64_t* seq_kv, int32_t n_blocks, cpattn_dtype_t dtype,
+                                      int32_t batch, int64_t seq_q, int32_t heads_q, int32_t heads_kv,
+                                      int32_t head_dim, const int64_t* q_positions, float scale,
+                                      float* out, float* lse, void* stream);
+
+/*
  * cpattn_lse_merge -- fold one completed partial result into an accumulator, in place.
  * [CP] "Peer-to-peer" (merging attention tiles) and [HB] "Ring Attention":
  *

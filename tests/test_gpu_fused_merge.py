@@ -39,8 +39,8 @@ def test_fused_ring_share_equals_tile_then_merge(dtype, C, t, Hq, Hkv, B):
     vs = [_rand(200 + o, (B, 2 * t, Hkv, D), dtype).to(DEV) for o in range(C)]
     for r in range(C):
         q = _rand(300 + r, (B, 2 * t, Hq, D), dtype).to(DEV)
-        fo, fl = cp.ring_share_fwd(q, ks, vs, pos, r, 1 / math.sqrt(D), fused=True)
-        uo, ul = cp.ring_share_fwd(q, ks, vs, pos, r, 1 / math.sqrt(D), fused=False)
+        fo, fl = cp.ring_share_fwd(q, ks, vs, pos, r, 1 / math.sqrt(D), mode="fused")
+        uo, ul = cp.ring_share_fwd(q, ks, vs, pos, r, 1 / math.sqrt(D), mode="unfused")
         torch.cuda.synchronize()
         assert _same_bits(fo, uo) and _same_bits(fl, ul), f"rank {r}"
 
