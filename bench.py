@@ -2,13 +2,16 @@
 """Benchmark: causal-attention TFLOP/s of one context-parallel rank's share on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                    [--mode single|fused|unfused] [--pass fwd|bwd]
 
 A step is one pass of the whole hot path over one batch of synthetic input already resident
 in HBM.  For the default workload (ring_share_256k: S=262144, C=8 zigzag, rank 3, 32 query /
 8 KV heads, D=128, bf16) that is: the zigzag positions of every owner, then for each of the
 8 ring steps one block attention of the rank's 32768 local queries against the owner's
-32768-token K/V shard; steps 1..7 fold their result into the accumulator by the LSE merge in
-the attention kernel's epilogue (``--unfused``: a separate merge kernel after each step).
+32768-token K/V shard, all in ONE launch that walks the 8 blocks in ring order with one running
+softmax per row, which folds the blocks together as the LSE merge would (``--mode fused``: one
+launch per step, merging in the epilogue; ``--mode unfused``: per-step tiles and the merge
+kernel).  ``--pass bwd`` times the ring-share backward instead.
 
 The value is whole-job throughput in TFLOP/s counting unmasked FLOPs only: 4*D FLOPs per
 visible (query, key) pair and query head (two matrix products; softmax not counted).
