@@ -40,7 +40,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_AS __attribute__((address_space(3)))
-#define GLOBAL_AS __attribute__((address_space(1)))
 
 constexpr int kD = 128;
 constexpr int kRowBytes = kD * 2;
@@ -102,8 +101,15 @@ __device__ inline bf16x8 lds_tr_pair(const LDS_AS char* p0, const LDS_AS char* p
     return __builtin_bit_cast(bf16x8, c);
 }
 
-__device__ inline void load_lds16(const void* g, LDS_AS void* lds_base) {
-    __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)g, lds_base, 16, 0, 0);
+// Buffer descriptor over `bytes` bytes from `base` (raw, no stride; word 3 as gfx9 wants).
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+// One 16-byte direct load into LDS: this lane's 16 bytes come from the descriptor's base +
+// voff and land at lds_base + 16*lane.  A buffer load, unlike global_load_lds, is not a flat
+// access, so LDS reads issued while it is in flight keep exact lgkm counts.
+__device__ inline void load_lds16(__amdgpu_buffer_rsrc_t r, uint32_t voff, LDS_AS void* lds_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_base, 16, voff, 0, 0, 0);
 }
 
 __device__ inline bf16x8 load_row16(const __bf16* p, bool valid) {
@@ -229,13 +235,17 @@ __global__ void __launch_bounds__(kThreads, 1) block_bwd_dq_kernel(const BwdPara
         const char* kb_t = kbase + (int64_t)jt * tile_bytes_g;
         const char* vb_t = vbase + (int64_t)jt * tile_bytes_g;
         const int64_t rmax = p.seq_kv - 1 - (int64_t)jt * kTile;  // last valid row of the tile
+        // the descriptors cover the tile's rows that exist (a tile spans < 4 GiB)
+        const uint32_t span = (uint32_t)((rmax < kTile - 1 ? rmax : kTile - 1) * kvstride * 2 + kRowBytes);
+        const __amdgpu_buffer_rsrc_t kr = make_rsrc(kb_t, span);
+        const __amdgpu_buffer_rsrc_t vr = make_rsrc(vb_t, span);
 #pragma unroll
         for (int i = 0; i < kLoads; ++i) {
             const int row = w * kRowsPerWave + 4 * i + ld_row_in;
             // rows past the end re-read the last key (finite data the mask hides)
             const uint32_t back = (row > rmax) ? (uint32_t)((row - rmax) * kvstride * 2) : 0u;
-            load_lds16(kb_t + koff[i] - back, kt + (w * kRowsPerWave + 4 * i) * kRowBytes);
-            load_lds16(vb_t + koff[i] - back, vt + (w * kRowsPerWave + 4 * i) * kRowBytes);
+            load_lds16(kr, koff[i] - back, kt + (w * kRowsPerWave + 4 * i) * kRowBytes);
+            load_lds16(vr, koff[i] - back, vt + (w * kRowsPerWave + 4 * i) * kRowBytes);
         }
     };
 
@@ -468,13 +478,16 @@ __global__ void __launch_bounds__(kThreads, 1) block_bwd_dkdv_kernel(const BwdPa
         const char* qb_t = (const char*)(p.q + (b * p.seq_q * p.heads_q + h) * (int64_t)kD) + qt * qtile_bytes_g;
         const char* gb_t = (const char*)(p.dout + (b * p.seq_q * p.heads_q + h) * (int64_t)kD) + qt * qtile_bytes_g;
         const int64_t rmax = p.seq_q - 1 - qt * kTile;
+        const uint32_t span = (uint32_t)((rmax < kTile - 1 ? rmax : kTile - 1) * qstride * 2 + kRowBytes);
+        const __amdgpu_buffer_rsrc_t qr = make_rsrc(qb_t, span);
+        const __amdgpu_buffer_rsrc_t gr = make_rsrc(gb_t, span);
 #pragma unroll
         for (int ii = 0; ii < kLoads; ++ii) {
             const int row = w * kRowsPerWave + 4 * ii + ld_row_in;
             // rows past the end re-read the last query; their lse is +inf, so p = 0
             const uint32_t back = (row > rmax) ? (uint32_t)((row - rmax) * qstride * 2) : 0u;
-            load_lds16(qb_t + qoff[ii] - back, st + (w * kRowsPerWave + 4 * ii) * kRowBytes);
-            load_lds16(gb_t + qoff[ii] - back, st + kTileBytes + (w * kRowsPerWave + 4 * ii) * kRowBytes);
+            load_lds16(qr, qoff[ii] - back, st + (w * kRowsPerWave + 4 * ii) * kRowBytes);
+            load_lds16(gr, qoff[ii] - back, st + kTileBytes + (w * kRowsPerWave + 4 * ii) * kRowBytes);
         }
     };
     // lse (log2 domain, +inf past the end or for rows with no visible key) and D of a step,

@@ -29,9 +29,12 @@
 //   O^T += V^T P^T with A = 32 dims x 16 keys of V read transposed from the row-major LDS
 //                  tile by ds_read_b64_tr_b16, B = P^T (registers).  The key order inside a
 //                  16-key step is the accumulator's own order, applied to V's addresses.
-// K and V tiles go from global memory straight into LDS (global_load_lds_dwordx4; each lane
-// lands 16 bytes at base + 16*lane, so the XOR-swizzled layout is chosen by which chunk each
-// lane fetches).  Two LDS stages: the next tile is in flight while the current one is used.
+// K and V tiles go from global memory straight into LDS (buffer_load_dwordx4 ... lds; each
+// lane lands 16 bytes at base + 16*lane, so the XOR-swizzled layout is chosen by which chunk
+// each lane fetches).  Two LDS stages: the next tile is in flight while the current one is
+// used.  Buffer loads rather than global_load_lds: the compiler treats a pending global LDS
+// load as a flat access and then waits for every outstanding LDS read (lgkmcnt(0)) before
+// each product, instead of only for the read the product needs.
 //
 // Causal skip ("Context parallelism: Ring Attention and Ulysses", Ring Attention: blocks
 // later than the query are skipped whole): with strictly increasing positions the visible
@@ -54,7 +57,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_AS __attribute__((address_space(3)))
-#define GLOBAL_AS __attribute__((address_space(1)))
 
 constexpr int kD = 128;             // head dim
 constexpr int kBN = 64;             // keys per tile
@@ -121,9 +123,15 @@ __device__ inline bf16x8 lds_tr_pair(const LDS_AS char* p0, const LDS_AS char* p
     return __builtin_bit_cast(bf16x8, c);
 }
 
-// One 16-byte direct global->LDS load: this lane's 16 bytes land at lds_base + 16*lane.
-__device__ inline void load_lds16(const void* g, LDS_AS void* lds_base) {
-    __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)g, lds_base, 16, 0, 0);
+// Buffer descriptor over `bytes` bytes from `base` (raw, no stride; word 3 as gfx9 wants).
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+// One 16-byte direct load into LDS through a buffer descriptor: this lane's 16 bytes come from
+// base + voff and land at lds_base + 16*lane.  (A buffer load, unlike a global one, is not a
+// flat access, so LDS reads issued while it is in flight keep exact lgkm counts.)
+__device__ inline void load_lds16(__amdgpu_buffer_rsrc_t r, uint32_t voff, LDS_AS void* lds_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_base, 16, voff, 0, 0, 0);
 }
 
 // LDS operand reads kept in flight ahead of the matrix products (K: one read per MFMA,
@@ -237,20 +245,25 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
         const char* kb_t = kbase_of(o) + (int64_t)jt * tile_bytes_g;
         const char* vb_t = vbase_of(o) + (int64_t)jt * tile_bytes_g;
         const int64_t seq_o = p.blk[o].seq;
+        // the descriptor covers this tile's rows that exist (a tile spans < 4 GiB)
+        const int64_t rows = seq_o - (int64_t)jt * kBN < kBN ? seq_o - (int64_t)jt * kBN : kBN;
+        const uint32_t span = (uint32_t)((rows - 1) * kvstride * 2 + kRowBytes);
+        const __amdgpu_buffer_rsrc_t kr = make_rsrc(kb_t, span);
+        const __amdgpu_buffer_rsrc_t vr = make_rsrc(vb_t, span);
         if ((int64_t)(jt + 1) * kBN <= seq_o) {
 #pragma unroll
             for (int i = 0; i < kLoadsPerWave; ++i) {
-                load_lds16(kb_t + koff[i], kt + (w * kRowsPerWave + 4 * i) * kRowBytes);
-                load_lds16(vb_t + voff[i], vt + (w * kRowsPerWave + 4 * i) * kRowBytes);
+                load_lds16(kr, koff[i], kt + (w * kRowsPerWave + 4 * i) * kRowBytes);
+                load_lds16(vr, voff[i], vt + (w * kRowsPerWave + 4 * i) * kRowBytes);
             }
         } else {
 #pragma unroll
             for (int i = 0; i < kLoadsPerWave; ++i) {
                 const int row = w * kRowsPerWave + 4 * i + ld_row_in;
                 const int64_t j = (int64_t)jt * kBN + row;
-                const int64_t over = (j >= seq_o) ? (j - (seq_o - 1)) * kvstride * 2 : 0;
-                load_lds16(kb_t + koff[i] - over, kt + (w * kRowsPerWave + 4 * i) * kRowBytes);
-                load_lds16(vb_t + voff[i] - over, vt + (w * kRowsPerWave + 4 * i) * kRowBytes);
+                const uint32_t over = (j >= seq_o) ? (uint32_t)((j - (seq_o - 1)) * kvstride * 2) : 0u;
+                load_lds16(kr, koff[i] - over, kt + (w * kRowsPerWave + 4 * i) * kRowBytes);
+                load_lds16(vr, voff[i] - over, vt + (w * kRowsPerWave + 4 * i) * kRowBytes);
             }
         }
     };
