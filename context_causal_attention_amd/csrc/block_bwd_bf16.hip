@@ -491,7 +491,9 @@ __global__ void __launch_bounds__(kThreads, 1) block_bwd_dkdv_kernel(const BwdPa
         }
     };
     // lse (log2 domain, +inf past the end or for rows with no visible key) and D of a step,
-    // one value per thread of the first two waves, fetched a step ahead through registers
+    // one value per thread of the first two waves, fetched a step ahead through registers.
+    // The raw value is converted only when it is stored at the end of the step, so that the
+    // wave does not wait for the load (and the tile loads issued before it) at the start.
     auto fetch_rowvals = [&](int u) -> float {
         int64_t h, qt;
         step_of(u, h, qt);
@@ -499,13 +501,11 @@ __global__ void __launch_bounds__(kThreads, 1) block_bwd_dkdv_kernel(const BwdPa
         const int64_t row = qt * kTile + r;
         if (tid >= 2 * kTile) return 0.f;
         const int64_t li = (b * p.heads_q + h) * p.seq_q + row;
-        if (tid < kTile) {
-            const float l = (row < p.seq_q) ? p.lse[li] : INFINITY;
-            return (l == -INFINITY) ? INFINITY : l * kLog2e;
-        }
+        if (tid < kTile) return (row < p.seq_q) ? p.lse[li] : INFINITY;
         return (row < p.seq_q) ? p.delta[li] : 0.f;
     };
     auto store_rowvals = [&](LDS_AS char* st, float x) {
+        if (tid < kTile) x = (x == -INFINITY) ? INFINITY : x * kLog2e;
         if (tid < 2 * kTile) ((LDS_AS float*)(st + 2 * kTileBytes))[tid] = x;
     };
 
