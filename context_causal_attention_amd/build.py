@@ -32,6 +32,16 @@ HIP_FLAGS = [
 ]
 
 
+# Per-file flags.  The backward kernels need more than 256 registers per lane; left to itself
+# the compiler then gives the matrix products accumulator-register (AGPR) destinations and
+# copies every score out of them for the vector math (v_accvgpr_read/write around each
+# product).  The vector-register form keeps the products' results where the vector
+# instructions read them; AGPRs then serve only as spill space.
+FILE_FLAGS = {
+    "block_bwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
+}
+
+
 def hipcc() -> str:
     for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if c and Path(c).exists():
@@ -45,7 +55,7 @@ def sources() -> list[Path]:
 
 def _compile(src: Path, verbose: bool, extra: list[str]) -> Path:
     obj = BUILD / (src.stem + ".o")
-    cmd = [hipcc(), *HIP_FLAGS, *extra, "-c", str(src), "-o", str(obj)]
+    cmd = [hipcc(), *HIP_FLAGS, *FILE_FLAGS.get(src.name, []), *extra, "-c", str(src), "-o", str(obj)]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

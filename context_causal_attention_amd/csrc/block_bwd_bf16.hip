@@ -135,14 +135,17 @@ __device__ inline void sched_reads_ahead() {
 }
 
 // Tiles in LDS are row-major (256 bytes per row) with 16-byte chunk c of row r stored at
-// chunk c ^ (r & 15): row reads of 16 consecutive rows are conflict-free, and transposed reads
-// of 4 rows by 16-lane groups stay within two passes.
+// chunk c ^ swz(r), swz(r) = ((r & 3) << 2) | ((r >> 2) & 3).  Over 16 aligned rows swz is a
+// permutation of 0..15, so a row read of 16 consecutive rows at one chunk touches 16 distinct
+// chunk slots; over 4 aligned rows its top two bits differ, so a transposed read of 4 rows x 4
+// chunks (one 32-lane pass) also touches 16 distinct slots.  Both are free of bank conflicts.
+__device__ inline int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 //
 // Row-read offsets (matrix-core A operand, 32 rows x 16 columns, lane = row l32 holding
 // columns 16*ks + 8*half .. +7): row l32 of a 32-row block.
 __device__ inline uint32_t row_off(int lane, int ks) {
     const int l32 = lane & 31, half = lane >> 5;
-    return l32 * kRowBytes + (((2 * ks + half) ^ (lane & 15)) << 4);
+    return l32 * kRowBytes + (((2 * ks + half) ^ swz(l32)) << 4);
 }
 // Transposed-read offsets (A operand = columns 32*db .. +31 as rows, 16 tile rows as k): the
 // k order is the accumulator's row order 16*ks2 + 8*(j/4) + 4*half + j%4, so that an operand
@@ -156,8 +159,8 @@ __device__ inline TrOff tr_off(int lane, int db) {
     const int vkey = 4 * half + (s16 >> 2);
     const int chunk = 4 * db + 2 * (grp & 1) + ((s16 & 3) >> 1);
     const uint32_t lo = (s16 & 1) << 3;
-    return TrOff{vkey * kRowBytes + ((chunk ^ vkey) << 4) + lo,
-                 (vkey + 8) * kRowBytes + ((chunk ^ (vkey + 8)) << 4) + lo};
+    return TrOff{vkey * kRowBytes + ((chunk ^ swz(vkey)) << 4) + lo,
+                 (vkey + 8) * kRowBytes + ((chunk ^ swz(vkey + 8)) << 4) + lo};
 }
 
 // ------------------------------------------------------------------------------------------
@@ -228,7 +231,7 @@ __global__ void __launch_bounds__(kThreads, 1) block_bwd_dq_kernel(const BwdPara
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
         const int row = w * kRowsPerWave + 4 * i + ld_row_in;
-        koff[i] = (uint32_t)(row * kvstride * 2) + ((ld_chunk ^ (row & 15)) << 4);
+        koff[i] = (uint32_t)(row * kvstride * 2) + ((ld_chunk ^ swz(row)) << 4);
     }
     auto issue_tile = [&](int jt, LDS_AS char* kt) {
         LDS_AS char* vt = kt + kTileBytes;
@@ -466,7 +469,7 @@ __global__ void __launch_bounds__(kThreads, 1) block_bwd_dkdv_kernel(const BwdPa
 #pragma unroll
     for (int ii = 0; ii < kLoads; ++ii) {
         const int row = w * kRowsPerWave + 4 * ii + ld_row_in;
-        qoff[ii] = (uint32_t)(row * qstride * 2) + ((ld_chunk ^ (row & 15)) << 4);
+        qoff[ii] = (uint32_t)(row * qstride * 2) + ((ld_chunk ^ swz(row)) << 4);
     }
     auto step_of = [&](int u, int64_t& h, int64_t& qt) {
         h = h0 + u / nq_vis;
