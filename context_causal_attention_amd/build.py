@@ -32,13 +32,16 @@ HIP_FLAGS = [
 ]
 
 
-# Per-file flags.  The backward kernels need more than 256 registers per lane; left to itself
-# the compiler then gives the matrix products accumulator-register (AGPR) destinations and
-# copies every score out of them for the vector math (v_accvgpr_read/write around each
-# product).  The vector-register form keeps the products' results where the vector
-# instructions read them; AGPRs then serve only as spill space.
+# Per-file flags.  Kernels allowed more than 256 registers per lane (one wave per SIMD: the
+# backward kernels and the forward's 4-wave variant) otherwise get accumulator-register (AGPR)
+# destinations for their matrix products, and every score is copied out of them for the
+# vector math (v_accvgpr_read/write around each product).  The vector-register form keeps the
+# products' results where the vector instructions read them; AGPRs then serve only as spill
+# space.  (The forward's 8-wave variant compiles to the same code either way.)
+_VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]
 FILE_FLAGS = {
-    "block_bwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
+    "block_bwd_bf16.hip": _VGPR_FORM,
+    "block_fwd_bf16.hip": _VGPR_FORM,
 }
 
 
