@@ -16,8 +16,12 @@ kernel).  ``--pass bwd`` times the ring-share backward instead.
 The value is whole-job throughput in TFLOP/s counting unmasked FLOPs only: 4*D FLOPs per
 visible (query, key) pair and query head (two matrix products; softmax not counted).
 The line also carries the roofline of the dominant kernel (block attention, measured with
-HIP events around each of its launches inside the timed steps) and the CPU oracle timed on
-a bounded sample of the same workload (``cpu_baseline``).
+HIP events around each of its launches inside the timed steps), the CPU oracle timed on
+a bounded sample of the same workload (``cpu_baseline``: its rate, the one-thread rate and the
+full share's time extrapolated from it), the bandwidth of the layout and merge kernels of the
+step (``hbm_kernels``, HIP events), the median and minimum step time, and the device
+(``device``: CU count and maximum clock as the device reports them, and the graphics clock
+read from the GPU metrics while the workload runs).
 
 One GPU only: --gpus above 1 exits with a message.
 """
@@ -111,7 +115,6 @@ class Plan:
             for rr in range(C):
                 pairs = 2 * C * t * t + t
                 self.attn_flops.append(4.0 * w.batch * w.heads_q * w.head_dim * pairs)
-            self.reorder_bytes = 2 * 2 * self.kg.numel() * self.kg.element_size()
         elif w.kind == "ulysses":
             s, g = w.local_len, w.group
             if w.zigzag:
@@ -137,8 +140,6 @@ class Plan:
             self.ost = torch.zeros((C, w.batch, s, w.heads_q, w.head_dim), dtype=torch.float32, device=dev)
             S = w.seq_len
             self.attn_flops.append(4.0 * w.batch * hq * w.head_dim * (S * (S + 1) // 2))
-            el = self.qst.element_size()
-            self.permute_bytes = 2 * (self.qg.numel() + 2 * self.kgp.numel()) * el + 2 * self.og.numel() * 4
         elif w.kind == "usp":
             A = w.a2a
             R = C // A
@@ -184,6 +185,7 @@ class Plan:
             self.attn_flops = [f * 2.5 for f in self.attn_flops]
             self.backward = True
         self.flops = sum(self.attn_flops)
+        self.hbm_ev = []  # (kernel, bytes, start, end) of the timed steps' bandwidth-bound kernels
 
     def step(self, ev=None):
         """Launch one step on the current stream.  ev: list to which (start, end) event
@@ -203,6 +205,17 @@ class Plan:
             else:
                 fn(*a)
 
+        def hbm(name, nbytes, fn, *a, **kw):
+            """A bandwidth-bound layout or merge kernel, timed when the step is timed."""
+            if ev is not None:
+                s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                s.record()
+                fn(*a, **kw)
+                e.record()
+                self.hbm_ev.append((name, nbytes, s, e))
+            else:
+                fn(*a, **kw)
+
         if self.kind == "ring_share":
             for o in range(C):
                 cp.zigzag_index(w.seq_len, C, o, out=self.pos[o])
@@ -221,29 +234,34 @@ class Plan:
                         attn(*a, self.out, self.lse, fn=cp.block_fwd_merge)
                     else:
                         attn(*a, self.tout, self.tlse)
-                        cp.lse_merge(self.out, self.lse, self.tout, self.tlse)
+                        hbm("lse_merge_kernel", 3 * (self.out.numel() + self.lse.numel()) * 4,
+                            cp.lse_merge, self.out, self.lse, self.tout, self.tlse)
         elif self.kind == "allgather":
-            cp.reorder_gathered(self.kg, C, cp.RANK_TO_SEQ, out=self.kseq)
-            cp.reorder_gathered(self.vg, C, cp.RANK_TO_SEQ, out=self.vseq)
+            nb = 2 * self.kg.numel() * self.kg.element_size()
+            hbm("reorder_kernel", nb, cp.reorder_gathered, self.kg, C, cp.RANK_TO_SEQ, out=self.kseq)
+            hbm("reorder_kernel", nb, cp.reorder_gathered, self.vg, C, cp.RANK_TO_SEQ, out=self.vseq)
             for rr in range(C):
                 cp.zigzag_index(w.seq_len, C, rr, out=self.pos[rr])
                 attn(self.qs[rr], self.kseq, self.vseq, self.pos[rr], self.gpos, w.scale, self.out, self.lse)
         elif self.kind == "ulysses":
             g, zz = w.group, w.zigzag
-            cp.ulysses_seq_to_heads(self.qst, g, out=self.qg, zigzag=zz)
-            cp.ulysses_seq_to_heads(self.kst, g, out=self.kgp, zigzag=zz)
-            cp.ulysses_seq_to_heads(self.vst, g, out=self.vgp, zigzag=zz)
+            nb = lambda x: 2 * x.numel() * x.element_size()  # noqa: E731  (read + write)
+            for src, dst in ((self.qst, self.qg), (self.kst, self.kgp), (self.vst, self.vgp)):
+                hbm("ulysses_kernel", nb(dst), cp.ulysses_seq_to_heads, src, g, out=dst, zigzag=zz)
             attn(self.qg, self.kgp, self.vgp, self.gpos, self.gpos, w.scale, self.og, self.lg)
-            cp.ulysses_heads_to_seq(self.og, g, self.ost, zigzag=zz)
+            hbm("ulysses_kernel", nb(self.og), cp.ulysses_heads_to_seq, self.og, g, self.ost, zigzag=zz)
         else:
             # the group's exchange for this rank's head group (every ring owner's K/V
             # exchange included, although on a mesh each group does its own), then the
             # ring over the R owners and the inverse exchange of the output
             R, g, a = self.R, self.g, self.a
-            cp.ulysses_seq_to_heads(self.qst, a, out=self.qh, zigzag=True)
+            nb = lambda x: 2 * x.numel() * x.element_size()  # noqa: E731  (read + write)
+            hbm("ulysses_kernel", nb(self.qh), cp.ulysses_seq_to_heads, self.qst, a, out=self.qh, zigzag=True)
             for o in range(R):
-                cp.ulysses_seq_to_heads(self.ksts[o], a, out=self.kh[o], zigzag=True)
-                cp.ulysses_seq_to_heads(self.vsts[o], a, out=self.vh[o], zigzag=True)
+                hbm("ulysses_kernel", nb(self.kh[o]), cp.ulysses_seq_to_heads, self.ksts[o], a, out=self.kh[o],
+                    zigzag=True)
+                hbm("ulysses_kernel", nb(self.vh[o]), cp.ulysses_seq_to_heads, self.vsts[o], a, out=self.vh[o],
+                    zigzag=True)
                 cp.zigzag_index(w.seq_len, R, o, out=self.pos[o])
             for step in range(R):
                 owner = (g - step) % R
@@ -252,7 +270,7 @@ class Plan:
                     attn(*a_, self.out, self.lse)
                 else:
                     attn(*a_, self.out, self.lse, fn=cp.block_fwd_merge)
-            cp.ulysses_heads_to_seq(self.out, a, self.ost, zigzag=True)
+            hbm("ulysses_kernel", nb(self.out), cp.ulysses_heads_to_seq, self.out, a, self.ost, zigzag=True)
 
 
     def step_bwd(self, ev=None):
@@ -260,7 +278,15 @@ class Plan:
         step (dq written at step 0 and added after; each owner's dk, dv written by its step)."""
         cp, torch, w = self.cp, self.torch, self.w
         C, r = w.cp_size, w.rank
-        cp.attn_bwd_delta(self.out, self.dout, self.delta)
+        nb = self.out.numel() * 4 + self.dout.numel() * self.dout.element_size() + self.delta.numel() * 4
+        if ev is not None:
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            cp.attn_bwd_delta(self.out, self.dout, self.delta)
+            e.record()
+            self.hbm_ev.append(("delta_kernel", nb, s, e))
+        else:
+            cp.attn_bwd_delta(self.out, self.dout, self.delta)
         q = self.qs[r]
         for step in range(C):
             owner = (r - step) % C
@@ -275,6 +301,85 @@ class Plan:
                 ev.append((s, e))
             else:
                 cp.block_bwd(*a)
+
+
+def _pci_bdf(index: int):
+    """PCI address of HIP device ``index`` ("0000:05:00.0"), or None."""
+    import ctypes
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        buf = ctypes.create_string_buffer(64)
+        if hip.hipDeviceGetPCIBusId(buf, 64, index) != 0:
+            return None
+        return buf.value.decode().lower()
+    except OSError:
+        return None
+
+
+def _hip_max_sclk_mhz(index: int):
+    """The device's maximum graphics clock (hipDeviceAttributeClockRate, kHz) in MHz, or None."""
+    import ctypes
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        v = ctypes.c_int(0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), 5, index) != 0 or v.value <= 0:
+            return None
+        return v.value / 1000.0
+    except OSError:
+        return None
+
+
+def sclk_under_load(plan, index: int, seconds: float = 2.0, settle: float = 1.0):
+    """Graphics clock of the benchmarked GPU while it runs this workload: the steps are
+    repeated (untimed) for ``seconds`` while a thread reads the per-XCD clocks from the amdsmi
+    GPU metrics every 50 ms; readings from the first ``settle`` seconds are dropped, since the
+    telemetry refreshes about once a second.  None-valued where the telemetry is unreadable."""
+    import threading
+    import torch
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+    except Exception as e:  # telemetry is optional
+        return {"mhz_mean": None, "note": f"amdsmi unavailable: {type(e).__name__}"}
+    try:
+        handles = amdsmi.amdsmi_get_processor_handles()
+        bdf = _pci_bdf(index)
+        match = [h for h in handles if bdf and str(amdsmi.amdsmi_get_gpu_device_bdf(h)).lower() == bdf]
+        h = match[0] if match else (handles[0] if len(handles) == 1 else None)
+        if h is None:
+            return {"mhz_mean": None, "note": "benchmarked GPU not found among amdsmi devices"}
+        samples, stop = [], threading.Event()
+        t0 = time.perf_counter()
+
+        def run():
+            while not stop.is_set():
+                if time.perf_counter() - t0 >= settle:
+                    try:
+                        xs = [float(x) for x in amdsmi.amdsmi_get_gpu_metrics_info(h)["current_gfxclks"]
+                              if isinstance(x, (int, float))]
+                        if xs:
+                            samples.append(xs)
+                    except Exception:
+                        pass
+                stop.wait(0.05)
+        th = threading.Thread(target=run, daemon=True)
+        th.start()
+        while time.perf_counter() - t0 < seconds:
+            plan.step()
+            torch.cuda.synchronize()
+        stop.set()
+        th.join()
+        if not samples:
+            return {"mhz_mean": None, "note": "no readings"}
+        per_xcd = [sum(col) / len(col) for col in zip(*samples)]
+        return {"mhz_mean": round(sum(per_xcd) / len(per_xcd), 1),
+                "mhz_per_xcd": [round(x) for x in per_xcd], "samples": len(samples),
+                "source": f"amdsmi GPU metrics current_gfxclks over {seconds - settle:.0f} s of extra untimed steps"}
+    finally:
+        try:
+            amdsmi.amdsmi_shut_down()
+        except Exception:
+            pass
 
 
 def profiled_traffic(workload: str, kernel: str):
@@ -295,7 +400,7 @@ def profiled_traffic(workload: str, kernel: str):
     return value if recorded == sha else None
 
 
-def cpu_baseline(w, budget_s: float):
+def cpu_baseline(w, budget_s: float, total_pairs: float):
     """The CPU oracle (as it stands) on a bounded sample of the same workload: direct causal
     attention of a seeded sample of the share's query rows, all heads, fp64."""
     import numpy as np
@@ -351,9 +456,25 @@ def cpu_baseline(w, budget_s: float):
     n = int(max(1, min(n_all, threads * budget_s / max(dt, 1e-3))))
     pairs, dt = run(n)
     flops = 4.0 * w.head_dim * pairs
+    # one thread on a few rows, for the per-core rate
+    rows1 = np.sort(rng.choice(n_all, size=2, replace=False)).astype(np.int64)
+    pairs1 = int(np.searchsorted(kvpos, qpos[rows1], side="right").sum()) * w.batch * heads
+    t0 = time.perf_counter()
+    oracle.attention_rows(q, k, v, qpos, kvpos, w.scale, rows=rows1, nthreads=1)
+    dt1 = time.perf_counter() - t0
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{n} of {n_all} local query rows (seeded), all {heads} query heads, "
-                      f"{pairs} visible pairs, fp64, {dt:.1f} s"}
+                      f"{pairs} visible pairs, fp64, {dt:.1f} s",
+            "pairs_per_s": pairs / dt, "pairs_per_s_1_thread": pairs1 / max(dt1, 1e-9), "cpu_model": model,
+            "extrapolated_full_share_s": total_pairs / (pairs / dt)}
 
 
 def main(argv=None) -> int:
@@ -384,14 +505,16 @@ def main(argv=None) -> int:
         plan.step()
     torch.cuda.synchronize()
     ev = []
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t_start.record()
-    for _ in range(args.steps):
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    marks[0].record()
+    for i in range(args.steps):
         plan.step(ev)
-    t_end.record()
+        marks[i + 1].record()
     torch.cuda.synchronize()
-    ms_total = t_start.elapsed_time(t_end)
+    sclk = sclk_under_load(plan, dev.index or 0)
+    ms_total = marks[0].elapsed_time(marks[-1])
     ms_step = ms_total / args.steps
+    ms_steps = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
     value = plan.flops / (ms_step * 1e-3) / 1e12
     attn_ms = [s.elapsed_time(e) for s, e in ev]
     attn_flops = plan.attn_flops * args.steps
@@ -400,6 +523,23 @@ def main(argv=None) -> int:
     bwd = args.which == "bwd"
     kernel = ("block_bwd_dq_kernel+block_bwd_dkdv_kernel" if bwd else "block_fwd_bf16_kernel") \
         if w.dtype == "bf16" else ("bwd_dq_f32_kernel+bwd_dkdv_f32_kernel" if bwd else "block_fwd_f32_kernel")
+    props = torch.cuda.get_device_properties(dev)
+    max_mhz = _hip_max_sclk_mhz(dev.index or 0)
+    device = {"name": props.name, "arch": props.gcnArchName, "cus": props.multi_processor_count,
+              "max_sclk_mhz": max_mhz or None,
+              # 4096 dense bf16 FLOPs per CU and clock: 256 CUs at 2.4 GHz give the published peak
+              "bf16_peak_from_device_tflops": round(props.multi_processor_count * 4096 * max_mhz * 1e6 / 1e12, 1)
+              if max_mhz else None,
+              "sclk_under_load": sclk}
+    hbm = {}
+    for name, nbytes, s_, e_ in plan.hbm_ev:
+        d = hbm.setdefault(name, [0, 0.0, 0.0])
+        d[0] += 1
+        d[1] += s_.elapsed_time(e_)
+        d[2] += nbytes
+    hbm_kernels = [{"kernel": k, "calls": c, "bytes_per_call": b / c, "avg_ms": round(ms / c, 4),
+                    "GB/s": round(b / (ms * 1e-3) / 1e9, 1), "frac_of_hbm_peak": round(b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+                   for k, (c, ms, b) in hbm.items()]
     result = {
         "metric": METRIC_BWD if bwd else METRIC,
         "value": round(value, 3),
@@ -408,6 +548,8 @@ def main(argv=None) -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "ms_per_step_median": round(ms_steps[len(ms_steps) // 2], 4),
+        "ms_per_step_min": round(ms_steps[0], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -425,11 +567,13 @@ def main(argv=None) -> int:
                      "traffic": profiled_traffic(w.name, "block_fwd_bf16_kernel") if w.dtype == "bf16" and not bwd
                      else None,
                      "avg_launch_ms": round(sum(attn_ms) / len(attn_ms), 4), "launches": len(attn_ms)},
+        "hbm_kernels": hbm_kernels,
+        "device": device,
     }
     if bwd:
         result["cpu_baseline"] = None  # the oracle baseline is quoted for the forward line
     elif not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, plan.flops / (4.0 * w.head_dim))
     print(json.dumps(result), flush=True)
     return 0
 
