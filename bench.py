@@ -61,6 +61,9 @@ def parse_args(argv=None):
                          "merging in its epilogue (fused), or per-step tiles plus the merge kernel")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step in a HIP graph and time its replays (for launch-bound "
+                         "small workloads); the attention launches are then timed as part of the step")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before the steps, run one plain chunk copy (reorder_gathered) of this "
                          "many MiB, as the reference dispatch for hardware byte counters")
@@ -506,9 +509,26 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     ev = []
     marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    graph = None
+    if args.graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            plan.step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            plan.step()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
     marks[0].record()
     for i in range(args.steps):
-        plan.step(ev)
+        if graph is not None:
+            graph.replay()
+        else:
+            plan.step(ev)
         marks[i + 1].record()
     torch.cuda.synchronize()
     sclk = sclk_under_load(plan, dev.index or 0)
@@ -516,7 +536,10 @@ def main(argv=None) -> int:
     ms_step = ms_total / args.steps
     ms_steps = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
     value = plan.flops / (ms_step * 1e-3) / 1e12
-    attn_ms = [s.elapsed_time(e) for s, e in ev]
+    if graph is not None:  # no events inside the graph: the whole step stands for its launches
+        attn_ms = [m / len(plan.attn_flops) for m in ms_steps for _ in plan.attn_flops]
+    else:
+        attn_ms = [s.elapsed_time(e) for s, e in ev]
     attn_flops = plan.attn_flops * args.steps
     achieved = sum(attn_flops) / (sum(attn_ms) * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
@@ -556,7 +579,7 @@ def main(argv=None) -> int:
         "dtype": w.dtype,
         "data": "synthetic (seeded iid N(0,1), per-chunk generators)",
         "config": {"workload": w.name + (f"_{args.mode}" if args.mode != "single" and w.kind == "ring_share" else "")
-                   + ("_bwd" if bwd else ""),
+                   + ("_bwd" if bwd else "") + ("_graph" if graph is not None else ""),
                    "batch": w.batch, "a2a": w.a2a, "zigzag": w.zigzag, "seq_len": w.seq_len, "cp_size": w.cp_size,
                    "rank": w.rank, "group": w.group, "heads_q": w.heads_q, "heads_kv": w.heads_kv,
                    "head_dim": w.head_dim, "unmasked_flops_per_step": plan.flops},
