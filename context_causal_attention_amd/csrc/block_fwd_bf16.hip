@@ -450,13 +450,14 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
             l_run[nb] += ts;
         }
 
-        // O^T += V^T P^T
+        // O^T += V^T P^T (the four accumulators interleaved: a product never waits on the one
+        // just issued)
 #pragma unroll
-        for (int db = 0; db < kD / 32; ++db) {
+        for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+            for (int ks2 = 0; ks2 < 2; ++ks2) {
 #pragma unroll
-                for (int ks2 = 0; ks2 < 2; ++ks2) {
+                for (int db = 0; db < kD / 32; ++db) {
                     const LDS_AS char* base = vt + (32 * kb + 16 * ks2) * kRowBytes + off_v[db];
                     const bf16x8 a = lds_tr_pair(base, base + 8 * kRowBytes);
 #pragma unroll
