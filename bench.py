@@ -61,6 +61,8 @@ def parse_args(argv=None):
                          "merging in its epilogue (fused), or per-step tiles plus the merge kernel")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--no-sclk", action="store_true",
+                    help="skip the clock reading (2 s of extra untimed steps after the timed ones)")
     ap.add_argument("--graph", action="store_true",
                     help="capture one step in a HIP graph and time its replays (for launch-bound "
                          "small workloads); the attention launches are then timed as part of the step")
@@ -531,7 +533,7 @@ def main(argv=None) -> int:
             plan.step(ev)
         marks[i + 1].record()
     torch.cuda.synchronize()
-    sclk = sclk_under_load(plan, dev.index or 0)
+    sclk = {"mhz_mean": None, "note": "skipped (--no-sclk)"} if args.no_sclk else sclk_under_load(plan, dev.index or 0)
     ms_total = marks[0].elapsed_time(marks[-1])
     ms_step = ms_total / args.steps
     ms_steps = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
