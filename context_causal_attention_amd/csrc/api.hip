@@ -154,6 +154,10 @@ CPATTN_API cpattn_status_t cpattn_attn_bwd_delta(const float* out, const void* d
     if (head_dim % 4 != 0)
         return fail(CPATTN_ERR_SHAPE, "attn_bwd_delta: head_dim %d not a multiple of 4", head_dim);
     if (!aligned16(out)) return fail(CPATTN_ERR_UNSUPPORTED, "attn_bwd_delta: out must be 16-byte aligned");
+    // dout is read four elements at a time: 16 bytes (fp32) or 8 bytes (bf16)
+    if ((uintptr_t)dout % (dtype == CPATTN_BF16 ? 8 : 16) != 0)
+        return fail(CPATTN_ERR_UNSUPPORTED, "attn_bwd_delta: dout must be %d-byte aligned",
+                    dtype == CPATTN_BF16 ? 8 : 16);
     if (((int64_t)batch * seq * heads * 16 + 255) / 256 > kMaxGrid)
         return fail(CPATTN_ERR_UNSUPPORTED, "attn_bwd_delta: launch grid too large");
     return from_hip(cpattn::launch_attn_bwd_delta(out, dout, dtype == CPATTN_BF16, batch, seq, heads, head_dim,
@@ -293,7 +297,7 @@ CPATTN_API cpattn_status_t cpattn_lse_merge(float* out, float* lse, const float*
         return fail(CPATTN_ERR_UNSUPPORTED, "lse_merge: out and out_tile must be 16-byte aligned");
     if (out == out_tile || lse == lse_tile)
         return fail(CPATTN_ERR_INVALID_ARG, "lse_merge: the tile must not alias the accumulator");
-    if (((int64_t)batch * seq * heads + 63) / 64 > kMaxGrid)
+    if (((int64_t)batch * seq * heads + 7) / 8 > kMaxGrid)  // 8 rows per block
         return fail(CPATTN_ERR_UNSUPPORTED, "lse_merge: launch grid too large");
     return from_hip(cpattn::launch_lse_merge(out, lse, out_tile, lse_tile, batch, seq, heads, head_dim,
                                              (hipStream_t)stream),
@@ -316,7 +320,7 @@ CPATTN_API cpattn_status_t cpattn_reorder_gathered(const void* in, void* out, in
     if (2LL * cp_size > 65535 || batch > 65535)
         return fail(CPATTN_ERR_UNSUPPORTED, "reorder_gathered: cp_size or batch too large");
     const int64_t chunk_bytes = seq_len / (2 * (int64_t)cp_size) * row_bytes;
-    if (chunk_bytes / 1024 + 1 > kMaxGrid)
+    if (chunk_bytes / 256 + 1 > kMaxGrid)  // the byte path copies 256 bytes per block
         return fail(CPATTN_ERR_UNSUPPORTED, "reorder_gathered: chunk too large");
     return from_hip(cpattn::launch_reorder_gathered(in, out, batch, seq_len, row_bytes, cp_size, (int32_t)dir,
                                                     (hipStream_t)stream),

@@ -10,6 +10,7 @@
 //   broadcast.  dk/dv kernel: one lane per key row (k, v, dk, dv in registers); Q/dout tiles
 //   of every query head of the group in LDS.  Only tiles with a visible pair are visited.
 #include "cpattn_internal.h"
+#include "stream_access.h"
 
 #include <math.h>
 
@@ -30,7 +31,11 @@ template <>
 __device__ inline float4 load4<float>(const float* p) { return *(const float4*)p; }
 template <>
 __device__ inline float4 load4<__bf16>(const __bf16* p) {
-    return make_float4((float)p[0], (float)p[1], (float)p[2], (float)p[3]);
+    // four bf16 in one 8-byte streaming read; a bf16 is the top half of the fp32 it widens to
+    const uint64_t u = __builtin_nontemporal_load((const uint64_t*)p);
+    const uint32_t lo = (uint32_t)u, hi = (uint32_t)(u >> 32);  // elements 0,1 and 2,3
+    return make_float4(__uint_as_float(lo << 16), __uint_as_float(lo & 0xFFFF0000u), __uint_as_float(hi << 16),
+                       __uint_as_float(hi & 0xFFFF0000u));
 }
 
 template <typename T>
@@ -44,7 +49,8 @@ __global__ void __launch_bounds__(256) delta_kernel(const float* __restrict__ ou
         const float* o = out + r * D;
         const T* g = dout + r * D;
         for (int d = 4 * sub; d < D; d += 64) {
-            const float4 a = *(const float4*)(o + d);
+            const v4f a4 = load_stream((const v4f*)(o + d));
+            const float4 a = make_float4(a4.x, a4.y, a4.z, a4.w);
             const float4 b = load4<T>(g + d);
             s = fmaf(a.x, b.x, s);
             s = fmaf(a.y, b.y, s);

@@ -2,10 +2,12 @@
 // arithmetic of merge_math.h ("On Context Parallelism", section Peer-to-peer).
 //
 // Bandwidth-bound: per row of head_dim floats it reads out and out_tile and writes out.
-// A block owns ROWS consecutive (b, i, h) rows: it first turns their lse pairs into the two
-// weights (in LDS), then streams the rows with 16-byte accesses.
+// A block owns kRows consecutive (b, i, h) rows: it first turns their lse pairs into the two
+// weights (in LDS), then streams the rows with 16-byte non-temporal accesses, one per lane
+// (stream_access.h).
 #include "cpattn_internal.h"
 #include "merge_math.h"
+#include "stream_access.h"
 
 #include <math.h>
 
@@ -13,7 +15,7 @@ namespace cpattn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRows = 64;
+constexpr int kRows = 8;   // 8 rows x 128 floats = one 16-byte access per lane
 
 __global__ void __launch_bounds__(kThreads) lse_merge_kernel(
     float* __restrict__ out, float* __restrict__ lse, const float* __restrict__ out_t,
@@ -38,18 +40,18 @@ __global__ void __launch_bounds__(kThreads) lse_merge_kernel(
     const int vec_per_row = head_dim / 4;
     const int rows_here = (int)((n_rows - row0) < kRows ? (n_rows - row0) : kRows);
     const int n_vec = rows_here * vec_per_row;
-    float4* o4 = reinterpret_cast<float4*>(out + row0 * head_dim);
-    const float4* t4 = reinterpret_cast<const float4*>(out_t + row0 * head_dim);
+    v4f* o4 = reinterpret_cast<v4f*>(out + row0 * head_dim);
+    const v4f* t4 = reinterpret_cast<const v4f*>(out_t + row0 * head_dim);
     for (int e = tid; e < n_vec; e += kThreads) {
         const int r = e / vec_per_row;
         const float a = w_old[r], c = w_new[r];
-        const float4 x = o4[e], y = t4[e];
-        float4 z;
+        const v4f x = load_stream(o4 + e), y = load_stream(t4 + e);
+        v4f z;
         z.x = merge_value(x.x, y.x, a, c);
         z.y = merge_value(x.y, y.y, a, c);
         z.z = merge_value(x.z, y.z, a, c);
         z.w = merge_value(x.w, y.w, a, c);
-        o4[e] = z;
+        store_stream(o4 + e, z);
     }
 }
 

@@ -5,15 +5,18 @@
 // for even k and chunk 2C-1-(k-1)/2 for odd k.
 //
 // A pure byte copy of B*2C contiguous chunks of t*row_bytes bytes each, bandwidth-bound:
-// each block copies a contiguous span of one destination chunk with 16-byte accesses
-// (byte accesses when sizes or pointers are not 16-byte aligned).  All offsets are 64-bit.
+// each block copies a contiguous span of one destination chunk, one 16-byte access per lane
+// (byte accesses when sizes or pointers are not 16-byte aligned); the 16-byte path streams
+// (stream_access.h).  All offsets are 64-bit.
 #include "cpattn_internal.h"
+#include "stream_access.h"
 
 namespace cpattn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kVecPerThread = 4;
+constexpr int kVecPerThread = 1;
+
 
 __device__ inline int64_t slot_of_chunk(int64_t c, int64_t C) {
     return c < C ? 2 * c : 2 * (2 * C - 1 - c) + 1;
@@ -37,12 +40,12 @@ __global__ void __launch_bounds__(kThreads) reorder_kernel(const T* __restrict__
 #pragma unroll
     for (int u = 0; u < kVecPerThread; ++u) {
         const int64_t e = base + (int64_t)u * kThreads;
-        if (e < chunk_elems) tmp[u] = s[e];
+        if (e < chunk_elems) tmp[u] = load_stream(s + e);
     }
 #pragma unroll
     for (int u = 0; u < kVecPerThread; ++u) {
         const int64_t e = base + (int64_t)u * kThreads;
-        if (e < chunk_elems) d[e] = tmp[u];
+        if (e < chunk_elems) store_stream(d + e, tmp[u]);
     }
 }
 
@@ -60,8 +63,8 @@ hipError_t launch_reorder_gathered(const void* in, void* out, int32_t batch, int
     const int64_t bx = (chunk_elems + per_block - 1) / per_block;
     const dim3 grid((unsigned)bx, (unsigned)(2 * cp_size), (unsigned)batch);
     if (vec)
-        hipLaunchKernelGGL(reorder_kernel<uint4>, grid, dim3(kThreads), 0, stream,
-                           (const uint4*)in, (uint4*)out, chunk_elems, seq_elems, cp_size, dir);
+        hipLaunchKernelGGL(reorder_kernel<v4u>, grid, dim3(kThreads), 0, stream,
+                           (const v4u*)in, (v4u*)out, chunk_elems, seq_elems, cp_size, dir);
     else
         hipLaunchKernelGGL(reorder_kernel<uint8_t>, grid, dim3(kThreads), 0, stream,
                            (const uint8_t*)in, (uint8_t*)out, chunk_elems, seq_elems, cp_size, dir);

@@ -14,16 +14,18 @@
 // For one (src, b) pair the move is a 2-D copy of s = S/C rows of one head-group segment
 // (H/C * D * elem bytes): in the stacked shards [C][B][S/C][H][D] the rows are H*D*elem
 // apart, in the grouped tensor [B][S][H/C][D] they are packed.  grid.y enumerates (src, b),
-// grid.x spans the s*seg elements of that copy.  Bandwidth-bound: 16-byte accesses when
-// sizes and pointers allow (byte accesses otherwise); the row/offset split uses a 32-bit
+// grid.x spans the s*seg elements of that copy.  Bandwidth-bound: one 16-byte streaming access
+// per lane when sizes and pointers allow (stream_access.h; byte accesses otherwise); the
+// row/offset split uses a 32-bit
 // division by an invariant divisor (multiply-high with a precomputed magic number).
 #include "cpattn_internal.h"
+#include "stream_access.h"
 
 namespace cpattn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kVecPerThread = 4;
+constexpr int kVecPerThread = 1;
 
 // Exact n / d for 0 <= n < 2^31 and 1 <= d < 2^31 (Granlund & Montgomery, "Division by
 // invariant integers using multiplication", 1994): l = ceil(log2 d),
@@ -65,8 +67,8 @@ __global__ void __launch_bounds__(kThreads) ulysses_kernel(const T* __restrict__
                              : ((int64_t)i < zz_t ? src * zz_t + i : (zz_last - src) * zz_t + (i - zz_t));
         const int64_t so = stacked_base + (int64_t)i * row + w;
         const int64_t go = grouped_b + grow * (int64_t)seg.d + w;
-        if (dir == 0) out[go] = in[so];
-        else out[so] = in[go];
+        if (dir == 0) store_stream(out + go, load_stream(in + so));
+        else store_stream(out + so, load_stream(in + go));
     }
 }
 
@@ -92,8 +94,8 @@ hipError_t launch_ulysses_permute(const void* in, void* out, int32_t elem_bytes,
     const int64_t zz_t = zigzag ? seq_len / (2 * (int64_t)cp_size) : 0;
     const int64_t zz_last = 2 * (int64_t)cp_size - 1;
     if (vec)
-        hipLaunchKernelGGL(ulysses_kernel<uint4>, grid, dim3(kThreads), 0, stream, (const uint4*)in,
-                           (uint4*)out, (uint32_t)span, fd, row_bytes / el, off_bytes / el, seq_len,
+        hipLaunchKernelGGL(ulysses_kernel<v4u>, grid, dim3(kThreads), 0, stream, (const v4u*)in,
+                           (v4u*)out, (uint32_t)span, fd, row_bytes / el, off_bytes / el, seq_len,
                            s, (int64_t)batch, dir, zz_t, zz_last);
     else
         hipLaunchKernelGGL(ulysses_kernel<uint8_t>, grid, dim3(kThreads), 0, stream,

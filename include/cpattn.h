@@ -211,7 +211,8 @@ cpattn_status_t cpattn_lse_merge(float* out, float* lse, const float* out_tile,
  *   dout   in  [batch][seq][heads][head_dim], dtype (bf16 or fp32)
  *   delta  out fp32 [batch][heads][seq]
  * Errors: INVALID_ARG (NULL pointer, sizes <= 0, seq < 0, bad dtype), SHAPE (head_dim % 4
- * != 0), UNSUPPORTED (out not 16-byte aligned).  seq == 0 is a no-op.
+ * != 0), UNSUPPORTED (out not 16-byte aligned, dout not 16-byte (fp32) or 8-byte (bf16)
+ * aligned).  seq == 0 is a no-op.
  */
 cpattn_status_t cpattn_attn_bwd_delta(const float* out, const void* dout, cpattn_dtype_t dtype,
                                       int32_t batch, int64_t seq, int32_t heads, int32_t head_dim,

@@ -147,3 +147,100 @@ def test_ulysses_zigzag_validation(lib):
     assert f(FAKE, other, 2, 1, 32, 8, 16, 4, 4, 0, NULL) == INVALID
     assert f(FAKE, FAKE, 2, 1, 32, 8, 16, 4, 0, 0, NULL) == INVALID
     assert f(FAKE, other, 2, 1, 32, 8, 16, 4, 0, 7, NULL) == INVALID
+
+
+def _delta(lib, **kw):
+    a = dict(out=FAKE, dout=FAKE, dtype=1, batch=1, seq=64, heads=4, d=128, delta=FAKE)
+    a.update(kw)
+    return lib.cpattn_attn_bwd_delta(a["out"], a["dout"], a["dtype"], a["batch"], a["seq"], a["heads"], a["d"],
+                                     a["delta"], NULL)
+
+
+def test_attn_bwd_delta_validation(lib):
+    assert _delta(lib, dtype=7) == INVALID
+    assert _delta(lib, batch=0) == INVALID
+    assert _delta(lib, heads=-1) == INVALID
+    assert _delta(lib, d=0) == INVALID
+    assert _delta(lib, seq=-1) == INVALID
+    assert _delta(lib, delta=NULL) == INVALID
+    assert _delta(lib, dout=NULL) == INVALID
+    assert _delta(lib, d=126) == SHAPE and "multiple of 4" in _err(lib)
+    assert _delta(lib, out=ctypes.c_void_p(0x1008)) == UNSUPPORTED
+    # dout is read four elements at a time: 8 bytes for bf16, 16 for fp32
+    # (an 8-byte aligned bf16 dout passes: the call then stops at the grid bound, before any launch)
+    assert _delta(lib, dout=ctypes.c_void_p(0x1008), dtype=1, seq=1 << 40) == UNSUPPORTED and "grid" in _err(lib)
+    assert _delta(lib, dout=ctypes.c_void_p(0x1004), dtype=1) == UNSUPPORTED and "8-byte" in _err(lib)
+    assert _delta(lib, dout=ctypes.c_void_p(0x1008), dtype=0) == UNSUPPORTED and "16-byte" in _err(lib)
+    assert _delta(lib, seq=0, out=NULL, dout=NULL, delta=NULL) == OK
+
+
+def _bb(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, dout=FAKE, dtype=1, batch=1, seq_q=64, seq_kv=64, hq=4, hkv=2, d=128,
+             qpos=FAKE, kvpos=FAKE, scale=0.1, lse=FAKE, delta=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, flags=0)
+    a.update(kw)
+    return lib.cpattn_block_bwd(a["q"], a["k"], a["v"], a["dout"], a["dtype"], a["batch"], a["seq_q"],
+                                a["seq_kv"], a["hq"], a["hkv"], a["d"], a["qpos"], a["kvpos"], a["scale"],
+                                a["lse"], a["delta"], a["dq"], a["dk"], a["dv"], a["flags"], NULL)
+
+
+def test_block_bwd_validation(lib):
+    assert _bb(lib, flags=4) == INVALID and "flags" in _err(lib)
+    assert _bb(lib, dtype=7) == INVALID
+    assert _bb(lib, batch=0) == INVALID
+    assert _bb(lib, hkv=0) == INVALID
+    assert _bb(lib, seq_q=-1) == INVALID
+    assert _bb(lib, seq_kv=-5) == INVALID
+    assert _bb(lib, scale=0.0) == INVALID
+    assert _bb(lib, scale=float("nan")) == INVALID
+    assert _bb(lib, hq=6, hkv=4) == SHAPE and "multiple" in _err(lib)
+    assert _bb(lib, d=96, dtype=0) == UNSUPPORTED
+    assert _bb(lib, d=64, dtype=1) == UNSUPPORTED  # bf16 path is D=128 only
+    for name in ("q", "k", "v", "dout", "qpos", "kvpos", "lse", "delta", "dq", "dk", "dv"):
+        assert _bb(lib, **{name: NULL}) == INVALID, name
+    for name in ("q", "k", "v", "dout", "dq", "dk", "dv"):
+        assert _bb(lib, **{name: ctypes.c_void_p(0x1004)}) == UNSUPPORTED, name
+    # no pair and nothing to overwrite: a no-op that never touches the GPU
+    assert _bb(lib, seq_q=0, q=NULL, dq=NULL, dk=NULL, dv=NULL) == OK
+    assert _bb(lib, seq_kv=0, k=NULL, v=NULL, dq=NULL, dk=NULL, dv=NULL) == OK
+    # overwriting an accumulator that exists needs its pointer
+    assert _bb(lib, seq_kv=0, flags=1, dq=NULL) == INVALID
+    assert _bb(lib, seq_q=0, flags=2, dv=NULL) == INVALID
+
+
+def _rs(lib, n=4, seqs=None, ks=None, vs=None, ps=None, **kw):
+    seqs = seqs if seqs is not None else [64] * n
+    ks = ks if ks is not None else [0x1000] * n
+    vs = vs if vs is not None else [0x1000] * n
+    ps = ps if ps is not None else [0x1000] * n
+    a = dict(q=FAKE, dtype=1, batch=1, seq_q=64, hq=4, hkv=2, d=128, qpos=FAKE, scale=0.1, out=FAKE, lse=FAKE,
+             n_blocks=n)
+    a.update(kw)
+    arr = ctypes.c_void_p * max(n, 1)
+    return lib.cpattn_ring_share_fwd(a["q"], arr(*ks), arr(*vs), arr(*ps), (ctypes.c_int64 * max(n, 1))(*seqs),
+                                     a["n_blocks"], a["dtype"], a["batch"], a["seq_q"], a["hq"], a["hkv"], a["d"],
+                                     a["qpos"], a["scale"], a["out"], a["lse"], NULL)
+
+
+def test_ring_share_fwd_validation(lib):
+    assert _rs(lib, n_blocks=0) == INVALID
+    assert _rs(lib, n=17) == INVALID and "n_blocks" in _err(lib)
+    assert _rs(lib, seqs=[64, -1, 64, 64]) == INVALID
+    assert _rs(lib, ks=[0x1000, 0, 0x1000, 0x1000]) == INVALID and "block 1" in _err(lib)
+    assert _rs(lib, ps=[0x1000, 0x1000, 0x1000, 0]) == INVALID
+    assert _rs(lib, vs=[0x1000, 0x1000, 0x1008, 0x1000]) == UNSUPPORTED and "block 2" in _err(lib)
+    # a block without keys may hold NULL pointers
+    assert _rs(lib, seqs=[64, 0, 64, 64], ks=[0x1000, 0, 0x1000, 0x1000], q=NULL, seq_q=0) == OK
+    assert _rs(lib, batch=0) == INVALID
+    assert _rs(lib, hq=0) == INVALID
+    assert _rs(lib, seq_q=-1) == INVALID
+    assert _rs(lib, scale=float("inf")) == INVALID
+    assert _rs(lib, hq=6, hkv=4) == SHAPE
+    assert _rs(lib, d=64) == UNSUPPORTED
+    for name in ("q", "qpos", "out", "lse"):
+        assert _rs(lib, **{name: NULL}) == INVALID, name
+    assert _rs(lib, q=ctypes.c_void_p(0x1004)) == UNSUPPORTED
+    assert _rs(lib, out=ctypes.c_void_p(0x1004)) == UNSUPPORTED
+    assert _rs(lib, seq_q=0, q=NULL, out=NULL, lse=NULL, qpos=NULL) == OK
+    # the fp32 path checks each block as a single-block call does
+    assert _rs(lib, dtype=0, d=96) == UNSUPPORTED
+    assert _rs(lib, dtype=0, hq=6, hkv=4) == SHAPE
