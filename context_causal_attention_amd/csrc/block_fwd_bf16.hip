@@ -11,9 +11,12 @@
 // (G = 4, 2 or 1, whichever divides heads_q/heads_kv) times PQ = 32*NW*NB/G query
 // positions.  Each wave owns NB column blocks of 32 query rows; every lane holds one query
 // row of each column block.  With NW = 8 two waves share a SIMD, so one wave's matrix
-// products overlap the other's softmax.
+// products overlap the other's softmax; with NW = 12, three.  At three waves per SIMD a wave
+// has 168 registers, too few for a whole tile's scores and weights, so that variant takes
+// each tile in two passes of 32 keys (KBP = 1 key block per pass; KBP = 2 is the whole
+// tile).  The first 8 waves (or all, when fewer) fill the LDS stages.
 //
-// Per K/V tile of 64 keys:
+// Per K/V tile of 64 keys (per pass of 32*KBP keys):
 //   S^T = K Q^T    with v_mfma_f32_32x32x16_bf16: A = 32 keys x 16 dims of K (LDS),
 //                  B = 16 dims x 32 queries of Q (registers, loaded once).  The accumulator
 //                  gives each lane 16 keys of ONE query, so the row max is lane-local plus
@@ -139,7 +142,7 @@ __device__ inline void load_lds16(__amdgpu_buffer_rsrc_t r, uint32_t voff, LDS_A
 constexpr int kReadAheadK = 4;
 constexpr int kReadAheadV = 2;
 
-template <int NW, int NB>
+template <int NW, int NB, int KBP>
 __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params p) {
     constexpr int kThreads = 64 * NW;
     // K/V tile row r, 16-byte chunk c is stored at chunk c ^ swz(r):
@@ -228,7 +231,8 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
     auto vbase_of = [&](int o) {
         return (const char*)(p.blk[o].v + (b * p.blk[o].seq * p.heads_kv + kvh) * (int64_t)kD);
     };
-    constexpr int kRowsPerWave = kBN / NW;
+    constexpr int kLW = NW < 8 ? NW : 8;  // waves that load (all, or the first 8)
+    constexpr int kRowsPerWave = kBN / kLW;
     constexpr int kLoadsPerWave = kRowsPerWave / 4;
     const int ld_row_in = lane >> 4;   // row within the 4-row slab
     const int ld_chunk = lane & 15;    // stored chunk
@@ -250,6 +254,7 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
         const uint32_t span = (uint32_t)((rows - 1) * kvstride * 2 + kRowBytes);
         const __amdgpu_buffer_rsrc_t kr = make_rsrc(kb_t, span);
         const __amdgpu_buffer_rsrc_t vr = make_rsrc(vb_t, span);
+        if (NW > kLW && w >= kLW) return;
         if ((int64_t)(jt + 1) * kBN <= seq_o) {
 #pragma unroll
             for (int i = 0; i < kLoadsPerWave; ++i) {
@@ -360,120 +365,124 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
         const LDS_AS char* vt = kt + kTileBytes;
         if (on < p.n_blk) issue_tile(on, jn, nxt);
 
-        // S^T = K Q^T
-        f32x16 s[NB][2];
+        // the tile in 2 / KBP passes of 32 * KBP keys each: scores, mask, softmax, PV
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            s[nb][0] = f32x16{};
-            s[nb][1] = f32x16{};
-        }
+        for (int ps = 0; ps < 2 / KBP; ++ps) {
+            // S^T = K Q^T
+            f32x16 s[NB][KBP];
 #pragma unroll
-        for (int ks = 0; ks < kD / 16; ++ks) {
+            for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const bf16x8 a = lds_b128(kt + kb * 32 * kRowBytes + off_k[ks]);
+                for (int kk = 0; kk < KBP; ++kk) s[nb][kk] = f32x16{};
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
-                    s[nb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[nb][ks], s[nb][kb], 0, 0, 0);
+            for (int ks = 0; ks < kD / 16; ++ks) {
+#pragma unroll
+                for (int kk = 0; kk < KBP; ++kk) {
+                    const bf16x8 a = lds_b128(kt + (ps * KBP + kk) * 32 * kRowBytes + off_k[ks]);
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+                        s[nb][kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[nb][ks], s[nb][kk], 0, 0, 0);
+                }
             }
-        }
-        // keep the operand reads kReadAheadK ahead of the matrix products
-        __builtin_amdgcn_sched_group_barrier(0x100, kReadAheadK, 1);
+            // keep the operand reads kReadAheadK ahead of the matrix products
+            __builtin_amdgcn_sched_group_barrier(0x100, kReadAheadK, 1);
 #pragma unroll
-        for (int i = 0; i < 16 - kReadAheadK; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, NB, 1);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, NB * kReadAheadK, 1);
+            for (int i = 0; i < 8 * KBP - kReadAheadK; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, NB, 1);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, NB * kReadAheadK, 1);
 
-        // element mask on tiles not entirely visible: key index of accumulator entry v is
-        // 32*kb + 8*(v/4) + 4*half + v%4 within the tile; visible iff below the row's count
-        if (jt >= n_full) {
+            // element mask on tiles not entirely visible: key index of accumulator entry v of
+            // key block kb is 32*kb + 8*(v/4) + 4*half + v%4 within the tile; visible iff below
+            // the row's count
+            if (jt >= n_full) {
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    const int64_t rel = vis[nb] - (int64_t)jt * kBN - 4 * half;
+                    const int lim = rel < 0 ? 0 : (rel > kBN ? kBN : (int)rel);
+#pragma unroll
+                    for (int kk = 0; kk < KBP; ++kk)
+#pragma unroll
+                        for (int v = 0; v < 16; ++v)
+                            if (32 * (ps * KBP + kk) + 8 * (v / 4) + v % 4 >= lim) s[nb][kk][v] = -INFINITY;
+                }
+            }
+
+            // softmax in the log2 domain against the running reference m.  Fast path: weights
+            // against the current m; they stay bounded (each at most 2^kLazy) whenever this
+            // lane's sum of them does, so no row max is needed.  Otherwise (or while m is unset)
+            // the wave takes the slow path: row max, raise m to it, rescale O and l, recompute.
+            bf16x8 pb[NB][KBP][2];
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                const int64_t rel = vis[nb] - (int64_t)jt * kBN - 4 * half;
-                const int lim = rel < 0 ? 0 : (rel > kBN ? kBN : (int)rel);
+                float m_use = (m_run[nb] == -INFINITY) ? 0.f : m_run[nb];
+                float ts = 0.f;
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v)
-                        if (32 * kb + 8 * (v / 4) + v % 4 >= lim) s[nb][kb][v] = -INFINITY;
-            }
-        }
-
-        // softmax in the log2 domain against the running reference m.  Fast path: weights
-        // against the current m; they stay bounded (each at most 2^kLazy) whenever this lane's
-        // sum of them does, so no row max is needed.  Otherwise (or while m is unset) the
-        // wave takes the slow path: row max, raise m to it, rescale O and l, recompute.
-        bf16x8 pb[NB][2][2];
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            float m_use = (m_run[nb] == -INFINITY) ? 0.f : m_run[nb];
-            float ts = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int h8 = 0; h8 < 2; ++h8)
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const float e = __builtin_amdgcn_exp2f(fmaf(s[nb][kb][8 * h8 + j], p.c, -m_use));
-                        ts += e;
-                        pb[nb][kb][h8][j] = (__bf16)e;
-                    }
-            const bool bad = !(ts <= kLazyWeight) || m_run[nb] == -INFINITY;
-            if (__builtin_amdgcn_ballot_w64(bad) != 0) {
-                float mx = -INFINITY;
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int vv = 0; vv < 16; ++vv) mx = fmaxf(mx, s[nb][kb][vv]);
-                const float mt = half_max(mx) * p.c;
-                const float m_new = fmaxf(m_run[nb], mt);
-                m_use = (m_new == -INFINITY) ? 0.f : m_new;
-                const float alpha = __builtin_amdgcn_exp2f(m_run[nb] - m_use);
-                l_run[nb] *= alpha;
-#pragma unroll
-                for (int db = 0; db < kD / 32; ++db) acc_o[nb][db] *= alpha;
-                m_run[nb] = m_new;
-                ts = 0.f;
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
+                for (int kk = 0; kk < KBP; ++kk)
 #pragma unroll
                     for (int h8 = 0; h8 < 2; ++h8)
 #pragma unroll
                         for (int j = 0; j < 8; ++j) {
-                            const float e = __builtin_amdgcn_exp2f(fmaf(s[nb][kb][8 * h8 + j], p.c, -m_use));
+                            const float e = __builtin_amdgcn_exp2f(fmaf(s[nb][kk][8 * h8 + j], p.c, -m_use));
                             ts += e;
-                            pb[nb][kb][h8][j] = (__bf16)e;
+                            pb[nb][kk][h8][j] = (__bf16)e;
                         }
+                const bool bad = !(ts <= kLazyWeight) || m_run[nb] == -INFINITY;
+                if (__builtin_amdgcn_ballot_w64(bad) != 0) {
+                    float mx = -INFINITY;
+#pragma unroll
+                    for (int kk = 0; kk < KBP; ++kk)
+#pragma unroll
+                        for (int vv = 0; vv < 16; ++vv) mx = fmaxf(mx, s[nb][kk][vv]);
+                    const float mt = half_max(mx) * p.c;
+                    const float m_new = fmaxf(m_run[nb], mt);
+                    m_use = (m_new == -INFINITY) ? 0.f : m_new;
+                    const float alpha = __builtin_amdgcn_exp2f(m_run[nb] - m_use);
+                    l_run[nb] *= alpha;
+#pragma unroll
+                    for (int db = 0; db < kD / 32; ++db) acc_o[nb][db] *= alpha;
+                    m_run[nb] = m_new;
+                    ts = 0.f;
+#pragma unroll
+                    for (int kk = 0; kk < KBP; ++kk)
+#pragma unroll
+                        for (int h8 = 0; h8 < 2; ++h8)
+#pragma unroll
+                            for (int j = 0; j < 8; ++j) {
+                                const float e = __builtin_amdgcn_exp2f(fmaf(s[nb][kk][8 * h8 + j], p.c, -m_use));
+                                ts += e;
+                                pb[nb][kk][h8][j] = (__bf16)e;
+                            }
+                }
+                l_run[nb] += ts;
             }
-            l_run[nb] += ts;
-        }
 
-        // O^T += V^T P^T (the four accumulators interleaved: a product never waits on the one
-        // just issued)
+            // O^T += V^T P^T (the four accumulators interleaved: a product never waits on the
+            // one just issued)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+            for (int kk = 0; kk < KBP; ++kk) {
 #pragma unroll
-            for (int ks2 = 0; ks2 < 2; ++ks2) {
+                for (int ks2 = 0; ks2 < 2; ++ks2) {
 #pragma unroll
-                for (int db = 0; db < kD / 32; ++db) {
-                    const LDS_AS char* base = vt + (32 * kb + 16 * ks2) * kRowBytes + off_v[db];
-                    const bf16x8 a = lds_tr_pair(base, base + 8 * kRowBytes);
+                    for (int db = 0; db < kD / 32; ++db) {
+                        const LDS_AS char* base = vt + (32 * (ps * KBP + kk) + 16 * ks2) * kRowBytes + off_v[db];
+                        const bf16x8 a = lds_tr_pair(base, base + 8 * kRowBytes);
 #pragma unroll
-                    for (int nb = 0; nb < NB; ++nb)
-                        acc_o[nb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[nb][kb][ks2], acc_o[nb][db], 0, 0, 0);
+                        for (int nb = 0; nb < NB; ++nb)
+                            acc_o[nb][db] =
+                                __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[nb][kk][ks2], acc_o[nb][db], 0, 0, 0);
+                    }
                 }
             }
-        }
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * kReadAheadV, 2);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * kReadAheadV, 2);
 #pragma unroll
-        for (int i = 0; i < 16 - kReadAheadV; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, NB, 2);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
+            for (int i = 0; i < 8 * KBP - kReadAheadV; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, NB, 2);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, NB * kReadAheadV, 2);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, NB * kReadAheadV, 2);
-
         // the next tile has landed in LDS (own loads) and every wave is done with this one
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), visible to the compiler
         __syncthreads();
@@ -546,12 +555,12 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
     }
 }
 
-template <int NW, int NB>
+template <int NW, int NB, int KBP>
 hipError_t launch_variant(Params p, int64_t seq_q, hipStream_t stream) {
     p.pq = 32 * NW * NB / p.G;
     p.n_qt = (seq_q + p.pq - 1) / p.pq;
     const int64_t blocks = p.n_qt * p.n_cols;
-    hipLaunchKernelGGL((block_fwd_bf16_kernel<NW, NB>), dim3((unsigned)blocks), dim3(64 * NW), 0, stream, p);
+    hipLaunchKernelGGL((block_fwd_bf16_kernel<NW, NB, KBP>), dim3((unsigned)blocks), dim3(64 * NW), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -576,11 +585,19 @@ hipError_t launch_block_fwd_bf16(const BlockFwdArgs& a, hipStream_t stream) {
     p.xcd_cols = (p.n_cols % 8 == 0) ? p.n_cols / 8 : 0;
     p.c = a.scale * kLog2e;
     p.merge = a.merge ? 1 : 0;
-    // 8 waves x 32 rows per block; 4 waves x 32 rows when that would leave the chip less
-    // than half full
+    // 4 waves x 32 rows when 8-wave blocks would leave the chip less than half full.
+    // Otherwise 12 waves (three per SIMD: more of each wave's softmax runs under the other
+    // waves' products, +3% on causal launches) when the blocks' work differs, i.e. the launch
+    // walks several K/V blocks or the queries and keys share one positions array (a causal
+    // triangle); the heavy blocks run first, so the last round of blocks is light.  Launches
+    // of equal-work blocks (queries against another shard's keys) keep 8 waves: 12-wave
+    // blocks hold 384/G positions (96 for G = 4), which split a power-of-two shard into a
+    // part-filled last round of the 256 CUs (8% slower measured on such ring steps), while
+    // 64-position blocks divide it evenly.
     const int64_t blocks8 = ((a.seq_q + 256 / p.G - 1) / (256 / p.G)) * p.n_cols;
-    if (blocks8 < 512) return launch_variant<4, 1>(p, a.seq_q, stream);
-    return launch_variant<8, 1>(p, a.seq_q, stream);
+    if (blocks8 < 512) return launch_variant<4, 1, 2>(p, a.seq_q, stream);
+    if (a.n_blk > 1 || a.blk[0].pos == a.q_pos) return launch_variant<12, 1, 1>(p, a.seq_q, stream);
+    return launch_variant<8, 1, 2>(p, a.seq_q, stream);
 }
 
 }  // namespace cpattn

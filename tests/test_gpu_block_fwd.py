@@ -118,3 +118,74 @@ def test_repeat_calls_are_identical():
     a = cp.block_fwd(q.to(DEV), k.to(DEV), v.to(DEV), pos, pos, 0.09)
     b = cp.block_fwd(q.to(DEV), k.to(DEV), v.to(DEV), pos, pos, 0.09)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def _rows(n: int, seed: int, extra: int = 24) -> np.ndarray:
+    """Rows to compare at launch sizes: both ends, rows around the 64- and 96-row block edges
+    at both ends, and seeded random rows."""
+    rng = np.random.default_rng(seed)
+    rows = {0, 1, 31, 32, 63, 64, 95, 96, 127, n - 97, n - 96, n - 65, n - 64, n - 33, n - 32, n - 2, n - 1}
+    rows.update(rng.integers(0, n, extra).tolist())
+    return np.array(sorted(r for r in rows if 0 <= r < n), dtype=np.int64)
+
+
+def _check_rows(out, lse, rows, ref_o, ref_l, what):
+    o = out[:, rows].cpu().numpy()
+    lv = lse[:, :, rows].cpu().numpy()
+    tol_o, tol_l = TOL["bf16"]
+    eo, el = max_abs(o, ref_o), max_abs(lv, ref_l)
+    assert eo <= tol_o and el <= tol_l, f"{what}: max abs err O {eo:.3g} lse {el:.3g}"
+
+
+# launches of at least 512 eight-wave blocks (the 8- and 12-wave kernels), ragged last
+# blocks, grouped-query ratios 4, 2 and 3: (B, S, Hq, Hkv)
+LARGE = [(1, 6000, 32, 8), (2, 4100, 32, 8), (1, 9000, 16, 8), (1, 11000, 12, 4)]
+
+
+@pytest.mark.parametrize("case", LARGE)
+def test_large_causal_launches(case):
+    """Causal self-attention at launch sizes: with one positions tensor for queries and keys
+    (the 12-wave kernel) and with the same positions in a second tensor (the 8-wave kernel);
+    sampled rows against the oracle."""
+    B, S, Hq, Hkv = case
+    D = 128
+    scale = 1 / math.sqrt(D)
+    q, k, v = _inputs(S % 997, B, S, S, Hq, Hkv, D, torch.bfloat16)
+    pos = np.arange(S, dtype=np.int64)
+    rows = _rows(S, S)
+    ref_o, ref_l = oracle.attention_rows(q.float().numpy(), k.float().numpy(), v.float().numpy(), pos, pos,
+                                         scale, rows=rows)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    tp = torch.from_numpy(pos).to(DEV)
+    for name, kvp in (("shared positions", tp), ("separate positions", tp.clone())):
+        out, lse = cp.block_fwd(qd, kd, vd, tp, kvp, scale)
+        torch.cuda.synchronize()
+        _check_rows(out, lse, rows, ref_o, ref_l, name)
+
+
+def test_large_zigzag_steps_and_share():
+    """A zigzag rank's queries at launch size (C = 4, t = 3000: 6000 local rows, 32/8 heads)
+    against an earlier, its own and a later owner's keys, one launch per step, and the whole
+    share in one launch; sampled rows against the oracle."""
+    C, t, Hq, Hkv, D = 4, 3000, 32, 8, 128
+    S, r = 2 * C * t, 1
+    scale = 1 / math.sqrt(D)
+    q_full, k_full, v_full = _inputs(77, 1, S, S, Hq, Hkv, D, torch.bfloat16)
+    pos = [oracle.zigzag_positions(S, C, o) for o in range(C)]
+    tpos = [torch.from_numpy(p).to(DEV) for p in pos]
+    q = q_full[:, pos[r]].contiguous().to(DEV)
+    ks = [k_full[:, p].contiguous().to(DEV) for p in pos]
+    vs = [v_full[:, p].contiguous().to(DEV) for p in pos]
+    rows = _rows(2 * t, 5)
+    qf, kf, vf = q_full.float().numpy(), k_full.float().numpy(), v_full.float().numpy()
+    for o in (0, r, C - 1):
+        ref_o, ref_l = oracle.attention_rows(qf[:, pos[r]], kf[:, pos[o]], vf[:, pos[o]], pos[r], pos[o], scale,
+                                             rows=rows)
+        out, lse = cp.block_fwd(q, ks[o], vs[o], tpos[r], tpos[o], scale)
+        torch.cuda.synchronize()
+        _check_rows(out, lse, rows, ref_o, ref_l, f"owner {o}")
+    gpos = np.arange(S, dtype=np.int64)
+    ref_o, ref_l = oracle.attention_rows(qf, kf, vf, gpos, gpos, scale, rows=pos[r][rows])
+    out, lse = cp.ring_share_fwd(q, ks, vs, tpos, r, scale)
+    torch.cuda.synchronize()
+    _check_rows(out, lse, rows, ref_o, ref_l, "one-launch share")
