@@ -67,8 +67,9 @@ def parse_args(argv=None):
                     help="capture one step in a HIP graph and time its replays (for launch-bound "
                          "small workloads); the attention launches are then timed as part of the step")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
-                    help="before the steps, run one plain chunk copy (reorder_gathered) of this "
-                         "many MiB, as the reference dispatch for hardware byte counters")
+                    help="before the steps, run one plain elementwise copy (torch.neg over fp32, "
+                         "cached loads and stores) of this many MiB, as the reference dispatch for "
+                         "hardware byte counters")
     return ap.parse_args(argv)
 
 
@@ -499,12 +500,13 @@ def main(argv=None) -> int:
     torch.cuda.set_device(dev)
     plan = Plan(w, dev, mode=args.mode, backward=args.which == "bwd")
     if args.copy_calibration_mib > 0:
-        import context_causal_attention_amd as cp
+        # the library's layout kernels stream with non-temporal accesses, which the byte
+        # counters report differently; the reference is a plain cached copy
         n = args.copy_calibration_mib << 20
-        src = torch.empty(n, dtype=torch.uint8, device=dev).view(1, 64, n // 64)
-        src.fill_(1)
-        cp.reorder_gathered(src, 4, cp.RANK_TO_SEQ)  # reads n bytes, writes n bytes
-        del src
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)  # reads n bytes, writes n bytes
+        del src, dst
     torch.cuda.synchronize()
     for _ in range(args.warmup):
         plan.step()
