@@ -17,11 +17,16 @@
 // of 64 keys are staged in LDS (direct global->LDS loads, two stages).  Per tile:
 //   S^T = K Q^T and dP^T = V dO^T (K, V rows read from LDS), p and ds per lane (one query:
 //   lse and D are per-lane scalars), dQ^T += K^T dS^T (K read transposed, ds_read_b64_tr_b16).
-// dk/dv kernel: a block of 4 waves owns 128 keys of one K/V head (32 per wave, one per lane,
-// k and v as matrix operands) and walks the query tiles of 64 rows that see them, for every
-// query head of the group.  Q, dO, lse and D tiles are staged in LDS.  Per 32-query half:
-//   S = Q K^T and dP = dO V^T (Q, dO rows from LDS), p and ds (lse and D per accumulator
+// dk/dv kernel: a block of 8 waves owns 128 keys of one K/V head, in 4 groups of 32 (one key
+// per lane; k as a matrix operand in registers, the block's v rows in LDS), and walks the
+// query tiles of 64 rows that see them, for every query head of the group.  Q, dO, lse and D
+// tiles are staged in LDS.  Each key group has two waves, one per 32-query half of every
+// tile, so two waves share each SIMD and one's products run beside the other's p/ds math.
+// Per wave and tile:
+//   S = Q K^T and dP = dO V^T (Q, dO, V rows from LDS), p and ds (lse and D per accumulator
 //   row, read from LDS), dV^T += dO^T P and dK^T += Q^T dS (Q, dO read transposed).
+// At the end the second-half waves hand their partial dK, dV to the first-half waves through
+// LDS, which add them and write the result.
 // The causal structure is used as in the forward: tiles entirely hidden are skipped, tiles
 // entirely visible need no mask, and partly visible tiles compare row indices with a count
 // found once by binary search over the positions.
@@ -379,15 +384,22 @@ __global__ void __launch_bounds__(kThreads, 1) block_bwd_dq_kernel(const BwdPara
 // dk/dv kernel
 // ------------------------------------------------------------------------------------------
 constexpr int kStageBytes = 2 * kTileBytes + 2 * kTile * 4;  // [Q | dO | lse2 | D]
+constexpr int kNWkv = 8;                       // dk/dv waves: 4 key groups x 2 query halves
+constexpr int kThreadsKv = 64 * kNWkv;
+constexpr int kRowsPerWaveKv = kTile / kNWkv;  // tile rows each wave loads
+constexpr int kLoadsKv = kRowsPerWaveKv / 4;
 
-__global__ void __launch_bounds__(kThreads, 1) block_bwd_dkdv_kernel(const BwdParams p) {
+__global__ void __launch_bounds__(kThreadsKv, 1) block_bwd_dkdv_kernel(const BwdParams p) {
     __shared__ __attribute__((aligned(16))) char lds_stage0[kStageBytes];
     __shared__ __attribute__((aligned(16))) char lds_stage1[kStageBytes];
-    __shared__ int red[2 * kNW];
+    __shared__ int red[2 * kNWkv];
+    __shared__ __attribute__((aligned(16))) char lds_v[4 * 32 * kRowBytes];  // the block's V rows
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int w = tid >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in a scalar register
+    const int kg = w & 3;   // key group: keys 32*kg .. +31 of the block
+    const int qhalf = w >> 2;  // the 32-row half of each query tile this wave takes
     const int half = lane >> 5;
     const int l32 = lane & 31;
 
@@ -415,7 +427,7 @@ __global__ void __launch_bounds__(kThreads, 1) block_bwd_dkdv_kernel(const BwdPa
     // query sees every key of the block (a shorter suffix, from qt_full)
     const int64_t n_qt = (p.seq_q + kTile - 1) / kTile;
     int c_hidden = 0, c_part = 0;
-    for (int64_t t = tid; t < n_qt; t += kThreads) {
+    for (int64_t t = tid; t < n_qt; t += kThreadsKv) {
         const int64_t lq = (t * kTile + kTile - 1 < p.seq_q) ? t * kTile + kTile - 1 : p.seq_q - 1;
         c_hidden += (p.qpos[lq] < kmin) ? 1 : 0;
         c_part += (p.qpos[t * kTile] < kmax) ? 1 : 0;
@@ -424,28 +436,33 @@ __global__ void __launch_bounds__(kThreads, 1) block_bwd_dkdv_kernel(const BwdPa
     c_part = wave_sum(c_part);
     if (lane == 0) {
         red[w] = c_hidden;
-        red[kNW + w] = c_part;
+        red[kNWkv + w] = c_part;
     }
     __syncthreads();
     int qt_lo = 0, qt_full = 0;
 #pragma unroll
-    for (int ii = 0; ii < kNW; ++ii) {
+    for (int ii = 0; ii < kNWkv; ++ii) {
         qt_lo += red[ii];
-        qt_full += red[kNW + ii];
+        qt_full += red[kNWkv + ii];
     }
     const int nq_vis = (int)n_qt - qt_lo;
     const int n_steps = nq_vis > 0 ? nq_vis * p.ratio : 0;  // (query head, query tile) pairs
     const int64_t h0 = (int64_t)kvh * p.ratio;
 
     // this lane's key row: k and v as B operands
-    const int64_t key = k0 + w * 32 + l32;
+    const int64_t key = k0 + kg * 32 + l32;
     const bool kvalid = key < p.seq_kv;
     const int64_t krow = (b * p.seq_kv + (kvalid ? key : 0)) * p.heads_kv + kvh;
-    bf16x8 kreg[kD / 16], vreg[kD / 16];
+    bf16x8 kreg[kD / 16];
 #pragma unroll
-    for (int ks = 0; ks < kD / 16; ++ks) {
-        kreg[ks] = load_row16(p.k + krow * kD + 16 * ks + 8 * half, kvalid);
-        vreg[ks] = load_row16(p.v + krow * kD + 16 * ks + 8 * half, kvalid);
+    for (int ks = 0; ks < kD / 16; ++ks) kreg[ks] = load_row16(p.k + krow * kD + 16 * ks + 8 * half, kvalid);
+    // V rows go to LDS once (the first-half waves write their key group's rows) and are read
+    // as the dP operand with the same swizzled row offsets as the Q and dO tiles
+    LDS_AS char* vl = (LDS_AS char*)lds_v + kg * 32 * kRowBytes;
+    if (qhalf == 0) {
+#pragma unroll
+        for (int ks = 0; ks < kD / 16; ++ks)
+            *(LDS_AS bf16x8*)(vl + row_off(lane, ks)) = load_row16(p.v + krow * kD + 16 * ks + 8 * half, kvalid);
     }
     // first query row that sees this key (rows before it are masked), when some tile is partial
     int64_t first = 0;
@@ -465,10 +482,10 @@ __global__ void __launch_bounds__(kThreads, 1) block_bwd_dkdv_kernel(const BwdPa
     const int64_t qtile_bytes_g = (int64_t)kTile * qstride * 2;
     const int ld_row_in = lane >> 4;
     const int ld_chunk = lane & 15;
-    uint32_t qoff[kLoads];
+    uint32_t qoff[kLoadsKv];
 #pragma unroll
-    for (int ii = 0; ii < kLoads; ++ii) {
-        const int row = w * kRowsPerWave + 4 * ii + ld_row_in;
+    for (int ii = 0; ii < kLoadsKv; ++ii) {
+        const int row = w * kRowsPerWaveKv + 4 * ii + ld_row_in;
         qoff[ii] = (uint32_t)(row * qstride * 2) + ((ld_chunk ^ swz(row)) << 4);
     }
     auto step_of = [&](int u, int64_t& h, int64_t& qt) {
@@ -485,12 +502,12 @@ __global__ void __launch_bounds__(kThreads, 1) block_bwd_dkdv_kernel(const BwdPa
         const __amdgpu_buffer_rsrc_t qr = make_rsrc(qb_t, span);
         const __amdgpu_buffer_rsrc_t gr = make_rsrc(gb_t, span);
 #pragma unroll
-        for (int ii = 0; ii < kLoads; ++ii) {
-            const int row = w * kRowsPerWave + 4 * ii + ld_row_in;
+        for (int ii = 0; ii < kLoadsKv; ++ii) {
+            const int row = w * kRowsPerWaveKv + 4 * ii + ld_row_in;
             // rows past the end re-read the last query; their lse is +inf, so p = 0
             const uint32_t back = (row > rmax) ? (uint32_t)((row - rmax) * qstride * 2) : 0u;
-            load_lds16(qr, qoff[ii] - back, st + (w * kRowsPerWave + 4 * ii) * kRowBytes);
-            load_lds16(gr, qoff[ii] - back, st + kTileBytes + (w * kRowsPerWave + 4 * ii) * kRowBytes);
+            load_lds16(qr, qoff[ii] - back, st + (w * kRowsPerWaveKv + 4 * ii) * kRowBytes);
+            load_lds16(gr, qoff[ii] - back, st + kTileBytes + (w * kRowsPerWaveKv + 4 * ii) * kRowBytes);
         }
     };
     // lse (log2 domain, +inf past the end or for rows with no visible key) and D of a step,
@@ -500,16 +517,17 @@ __global__ void __launch_bounds__(kThreads, 1) block_bwd_dkdv_kernel(const BwdPa
     auto fetch_rowvals = [&](int u) -> float {
         int64_t h, qt;
         step_of(u, h, qt);
-        const int r = tid & 63;
-        const int64_t row = qt * kTile + r;
-        if (tid >= 2 * kTile) return 0.f;
+        // wave 0 fetches lse, wave 1 D (kTile = 64 rows: one per lane); wave-uniform choices,
+        // so the base pointers stay scalar
+        const int64_t row = qt * kTile + lane;
+        if (w >= 2) return 0.f;
         const int64_t li = (b * p.heads_q + h) * p.seq_q + row;
-        if (tid < kTile) return (row < p.seq_q) ? p.lse[li] : INFINITY;
+        if (w == 0) return (row < p.seq_q) ? p.lse[li] : INFINITY;
         return (row < p.seq_q) ? p.delta[li] : 0.f;
     };
     auto store_rowvals = [&](LDS_AS char* st, float x) {
-        if (tid < kTile) x = (x == -INFINITY) ? INFINITY : x * kLog2e;
-        if (tid < 2 * kTile) ((LDS_AS float*)(st + 2 * kTileBytes))[tid] = x;
+        if (w == 0) x = (x == -INFINITY) ? INFINITY : x * kLog2e;
+        if (w < 2) ((LDS_AS float*)(st + 2 * kTileBytes))[tid] = x;
     };
 
     f32x16 dk[kD / 32], dv[kD / 32];
@@ -541,18 +559,19 @@ __global__ void __launch_bounds__(kThreads, 1) block_bwd_dkdv_kernel(const BwdPa
         int64_t h, qt;
         step_of(u, h, qt);
         const bool masked = qt < qt_full;
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+        {
+            const int qb = qhalf;
             // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys
             f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
             for (int ks = 0; ks < kD / 16; ++ks) {
                 const bf16x8 qa = lds_b128(qt_l + qb * 32 * kRowBytes + off_r[ks]);
                 const bf16x8 ga = lds_b128(gt_l + qb * 32 * kRowBytes + off_r[ks]);
+                const bf16x8 va = lds_b128(vl + off_r[ks]);
                 s = mfma(qa, kreg[ks], s);
-                dp = mfma(ga, vreg[ks], dp);
+                dp = mfma(ga, va, dp);
             }
-            sched_reads_ahead<8, 2, 2, 3>();
+            sched_reads_ahead<8, 2, 3, 3>();
             // entry v is query row qb*32 + 8*(v/4) + 4*half + v%4 of the tile, key l32
             const int64_t rel = first - qt * kTile - qb * 32 - 4 * half;
             const int lim = rel < 0 ? 0 : (rel > 32 ? 32 : (int)rel);
@@ -601,8 +620,31 @@ __global__ void __launch_bounds__(kThreads, 1) block_bwd_dkdv_kernel(const BwdPa
         if (u + 1 < n_steps) step(u + 1, st1, st0);
     }
 
+    // the two query halves' partial sums: the second-half waves hand theirs to the first-half
+    // waves through LDS (one tensor at a time; each stage holds two waves' 16 KB)
+    {
+        LDS_AS float* xch = (LDS_AS float*)((kg >> 1) ? lds_stage1 : lds_stage0) + (kg & 1) * (64 * 64);
+        auto combine = [&](f32x16(&acc)[kD / 32]) {
+            if (qhalf == 1) {
+#pragma unroll
+                for (int db = 0; db < kD / 32; ++db)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) xch[(db * 16 + v) * 64 + lane] = acc[db][v];
+            }
+            __syncthreads();
+            if (qhalf == 0) {
+#pragma unroll
+                for (int db = 0; db < kD / 32; ++db)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) acc[db][v] += xch[(db * 16 + v) * 64 + lane];
+            }
+            __syncthreads();
+        };
+        combine(dk);
+        combine(dv);
+    }
     // dk += scale * dK, dv += dV; entry v of block db is dimension 32*db + 8*(v/4) + 4*half + v%4
-    if (!kvalid) return;
+    if (!kvalid || qhalf != 0) return;
     float* krow_k = p.dk + krow * kD;
     float* krow_v = p.dv + krow * kD;
 #pragma unroll
@@ -663,7 +705,7 @@ hipError_t launch_block_bwd_bf16(const BlockBwdArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(block_bwd_dq_kernel, dim3((unsigned)(p.n_qt * p.n_cols)), dim3(kThreads), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(block_bwd_dkdv_kernel, dim3((unsigned)(p.n_kb * p.kv_cols)), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(block_bwd_dkdv_kernel, dim3((unsigned)(p.n_kb * p.kv_cols)), dim3(kThreadsKv), 0, stream, p);
     return hipGetLastError();
 }
 
