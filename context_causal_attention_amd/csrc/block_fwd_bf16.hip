@@ -16,6 +16,12 @@
 // each tile in two passes of 32 keys (KBP = 1 key block per pass; KBP = 2 is the whole
 // tile).  The first 8 waves (or all, when fewer) fill the LDS stages.
 //
+// Key split (KS = 2, for launches too small to fill the chip): the NW waves form KS groups of
+// NW/KS waves over the same rows.  Group g takes tiles g, g+KS, ... of the block's tile
+// sequence, with its own LDS stages, running softmax and accumulator; at the end the groups'
+// states meet in group 0, rescaled to the larger reference (the same exact combine as the
+// merge of two blocks), before the epilogue.
+//
 // Per K/V tile of 64 keys (per pass of 32*KBP keys):
 //   S^T = K Q^T    with v_mfma_f32_32x32x16_bf16: A = 32 keys x 16 dims of K (LDS),
 //                  B = 16 dims x 32 queries of Q (registers, loaded once).  The accumulator
@@ -142,22 +148,27 @@ __device__ inline void load_lds16(__amdgpu_buffer_rsrc_t r, uint32_t voff, LDS_A
 constexpr int kReadAheadK = 4;
 constexpr int kReadAheadV = 2;
 
-template <int NW, int NB, int KBP>
+template <int NW, int NB, int KBP, int KS>
 __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params p) {
+    static_assert(KS == 1 || NB == 1, "the key split combines one column block per wave");
     constexpr int kThreads = 64 * NW;
+    constexpr int NWR = NW / KS;  // waves per row group (all waves unless the keys are split)
     // K/V tile row r, 16-byte chunk c is stored at chunk c ^ swz(r):
     //   K: r & 15 (row reads by 16 consecutive keys are conflict-free)
     //   V: (r & 3) << 2 (transposed reads: each 32-lane half reads 4 consecutive keys x 64 B,
     //      which this spreads over all 64 banks)
     // two stages in two distinct arrays, so that the compiler can tell the stage being read
     // from the stage being filled and does not wait for the fill before reading
-    __shared__ __attribute__((aligned(16))) char lds_stage0[2 * kTileBytes];  // [K|V][tile]
-    __shared__ __attribute__((aligned(16))) char lds_stage1[2 * kTileBytes];
+    // (with the keys split over KS wave groups, each group has its own pair of stages)
+    __shared__ __attribute__((aligned(16))) char lds_stage0[KS * 2 * kTileBytes];  // [group][K|V][tile]
+    __shared__ __attribute__((aligned(16))) char lds_stage1[KS * 2 * kTileBytes];
     __shared__ int red[2 * NW];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int w = tid >> 6;
+    const int w = KS > 1 ? __builtin_amdgcn_readfirstlane(tid >> 6) : (tid >> 6);
+    const int wr = KS > 1 ? w % NWR : w;  // wave within its row group
+    const int ksg = KS > 1 ? w / NWR : 0;  // key group: takes tiles ksg, ksg + KS, ... of the sequence
     const int half = lane >> 5;
     const int l32 = lane & 31;
 
@@ -231,7 +242,7 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
     auto vbase_of = [&](int o) {
         return (const char*)(p.blk[o].v + (b * p.blk[o].seq * p.heads_kv + kvh) * (int64_t)kD);
     };
-    constexpr int kLW = NW < 8 ? NW : 8;  // waves that load (all, or the first 8)
+    constexpr int kLW = NWR < 8 ? NWR : 8;  // waves of a row group that load (all, or the first 8)
     constexpr int kRowsPerWave = kBN / kLW;
     constexpr int kLoadsPerWave = kRowsPerWave / 4;
     const int ld_row_in = lane >> 4;   // row within the 4-row slab
@@ -239,7 +250,7 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
     uint32_t koff[kLoadsPerWave], voff[kLoadsPerWave];
 #pragma unroll
     for (int i = 0; i < kLoadsPerWave; ++i) {
-        const int row = w * kRowsPerWave + 4 * i + ld_row_in;
+        const int row = wr * kRowsPerWave + 4 * i + ld_row_in;
         koff[i] = (uint32_t)(row * kvstride * 2) + ((ld_chunk ^ (row & 15)) << 4);
         voff[i] = (uint32_t)(row * kvstride * 2) + ((ld_chunk ^ ((row & 3) << 2)) << 4);
     }
@@ -254,21 +265,21 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
         const uint32_t span = (uint32_t)((rows - 1) * kvstride * 2 + kRowBytes);
         const __amdgpu_buffer_rsrc_t kr = make_rsrc(kb_t, span);
         const __amdgpu_buffer_rsrc_t vr = make_rsrc(vb_t, span);
-        if (NW > kLW && w >= kLW) return;
+        if (NWR > kLW && wr >= kLW) return;
         if ((int64_t)(jt + 1) * kBN <= seq_o) {
 #pragma unroll
             for (int i = 0; i < kLoadsPerWave; ++i) {
-                load_lds16(kr, koff[i], kt + (w * kRowsPerWave + 4 * i) * kRowBytes);
-                load_lds16(vr, voff[i], vt + (w * kRowsPerWave + 4 * i) * kRowBytes);
+                load_lds16(kr, koff[i], kt + (wr * kRowsPerWave + 4 * i) * kRowBytes);
+                load_lds16(vr, voff[i], vt + (wr * kRowsPerWave + 4 * i) * kRowBytes);
             }
         } else {
 #pragma unroll
             for (int i = 0; i < kLoadsPerWave; ++i) {
-                const int row = w * kRowsPerWave + 4 * i + ld_row_in;
+                const int row = wr * kRowsPerWave + 4 * i + ld_row_in;
                 const int64_t j = (int64_t)jt * kBN + row;
                 const uint32_t over = (j >= seq_o) ? (uint32_t)((j - (seq_o - 1)) * kvstride * 2) : 0u;
-                load_lds16(kr, koff[i] - over, kt + (w * kRowsPerWave + 4 * i) * kRowBytes);
-                load_lds16(vr, voff[i] - over, vt + (w * kRowsPerWave + 4 * i) * kRowBytes);
+                load_lds16(kr, koff[i] - over, kt + (wr * kRowsPerWave + 4 * i) * kRowBytes);
+                load_lds16(vr, voff[i] - over, vt + (wr * kRowsPerWave + 4 * i) * kRowBytes);
             }
         }
     };
@@ -280,7 +291,7 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
     int64_t mypos[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-        const int row0 = (w * NB + nb) * 32;
+        const int row0 = (wr * NB + nb) * 32;
         const int hs = row0 / p.pq;
         const int64_t i = q0 + (row0 % p.pq) + l32;
         const int64_t head = (int64_t)kvh * p.ratio + (int64_t)hg * p.G + hs;
@@ -347,8 +358,8 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
         off_v[db] = vkey * kRowBytes + ((chunk ^ vsw) << 4) + ((s16 & 1) << 3);
     }
 
-    LDS_AS char* st0 = (LDS_AS char*)lds_stage0;
-    LDS_AS char* st1 = (LDS_AS char*)lds_stage1;
+    LDS_AS char* st0 = (LDS_AS char*)lds_stage0 + ksg * 2 * kTileBytes;
+    LDS_AS char* st1 = (LDS_AS char*)lds_stage1 + ksg * 2 * kTileBytes;
 
     // cursors: the tile being computed (block oc, tile jt; n_full of oc) and the next one to
     // load (block on, tile jn; on == p.n_blk when there is none)
@@ -365,9 +376,10 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
         const LDS_AS char* vt = kt + kTileBytes;
         if (on < p.n_blk) issue_tile(on, jn, nxt);
 
-        // the tile in 2 / KBP passes of 32 * KBP keys each: scores, mask, softmax, PV
+        // the tile in 2 / KBP passes of 32 * KBP keys each: scores, mask, softmax, PV (with the
+        // keys split, a group whose share has run out only keeps the barriers)
 #pragma unroll
-        for (int ps = 0; ps < 2 / KBP; ++ps) {
+        for (int ps = 0; ps < ((KS == 1 || oc < p.n_blk) ? 2 / KBP : 0); ++ps) {
             // S^T = K Q^T
             f32x16 s[NB][KBP];
 #pragma unroll
@@ -487,8 +499,16 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), visible to the compiler
         __syncthreads();
         const int o_prev = oc;
-        advance(oc, jt);
-        if (on < p.n_blk) advance(on, jn);
+        if (KS == 1) {
+            advance(oc, jt);
+            if (on < p.n_blk) advance(on, jn);
+        } else {
+#pragma unroll
+            for (int s2 = 0; s2 < KS; ++s2) {
+                if (oc < p.n_blk) advance(oc, jt);
+                if (on < p.n_blk) advance(on, jn);
+            }
+        }
         if (oc != o_prev && oc < p.n_blk) {
             n_full = blk_full[oc];
             find_vis(oc);
@@ -496,19 +516,58 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
     };
 
     while (oc < p.n_blk && blk_ne[oc] == 0) ++oc;  // first block with a visible tile
+    // key group g starts at tile g of the sequence
+    for (int s2 = 0; s2 < ksg; ++s2)
+        if (oc < p.n_blk) advance(oc, jt);
     if (oc < p.n_blk) {
         n_full = blk_full[oc];
         find_vis(oc);
-        issue_tile(oc, 0, st0);
+        issue_tile(oc, jt, st0);
         on = oc;
-        jn = 0;
-        advance(on, jn);
+        jn = jt;
+        if (KS == 1) {
+            advance(on, jn);
+        } else {
+#pragma unroll
+            for (int s2 = 0; s2 < KS; ++s2)
+                if (on < p.n_blk) advance(on, jn);
+        }
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), visible to the compiler
     __syncthreads();
-    for (int u = 0; u < n_total; u += 2) {
+    const int n_it = (n_total + KS - 1) / KS;  // tiles per key group, rounded up
+    for (int u = 0; u < n_it; u += 2) {
         tile(st0, st1);
-        if (u + 1 < n_total) tile(st1, st0);
+        if (u + 1 < n_it) tile(st1, st0);
+    }
+
+    if constexpr (KS > 1) {
+        // the key groups' partial softmax states (accumulator, reference m, sums l) meet in
+        // group 0: group 1 hands its own over through LDS (the stages are free now) and group
+        // 0 rescales both to the larger reference
+        LDS_AS float* xa = (LDS_AS float*)lds_stage0 + wr * (16 * (kD / 32) * 64);
+        LDS_AS float* xm = (LDS_AS float*)lds_stage1 + wr * (2 * 64);
+        if (ksg == 1) {
+#pragma unroll
+            for (int db = 0; db < kD / 32; ++db)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) xa[(db * 16 + v) * 64 + lane] = acc_o[0][db][v];
+            xm[lane] = m_run[0];
+            xm[64 + lane] = l_run[0];
+        }
+        __syncthreads();
+        if (ksg != 0) return;
+        const float mb = xm[lane], lb = xm[64 + lane];
+        const float m = fmaxf(m_run[0], mb);
+        const float fa = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run[0] - m);
+        const float fb = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mb - m);
+        l_run[0] = l_run[0] * fa + lb * fb;
+#pragma unroll
+        for (int db = 0; db < kD / 32; ++db)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                acc_o[0][db][v] = acc_o[0][db][v] * fa + xa[(db * 16 + v) * 64 + lane] * fb;
+        m_run[0] = m;
     }
 
     // ---- epilogue: combine the half-wave row sums, normalise, store (or merge into out, lse)
@@ -555,12 +614,12 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
     }
 }
 
-template <int NW, int NB, int KBP>
+template <int NW, int NB, int KBP, int KS>
 hipError_t launch_variant(Params p, int64_t seq_q, hipStream_t stream) {
-    p.pq = 32 * NW * NB / p.G;
+    p.pq = 32 * (NW / KS) * NB / p.G;
     p.n_qt = (seq_q + p.pq - 1) / p.pq;
     const int64_t blocks = p.n_qt * p.n_cols;
-    hipLaunchKernelGGL((block_fwd_bf16_kernel<NW, NB, KBP>), dim3((unsigned)blocks), dim3(64 * NW), 0, stream, p);
+    hipLaunchKernelGGL((block_fwd_bf16_kernel<NW, NB, KBP, KS>), dim3((unsigned)blocks), dim3(64 * NW), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -585,8 +644,9 @@ hipError_t launch_block_fwd_bf16(const BlockFwdArgs& a, hipStream_t stream) {
     p.xcd_cols = (p.n_cols % 8 == 0) ? p.n_cols / 8 : 0;
     p.c = a.scale * kLog2e;
     p.merge = a.merge ? 1 : 0;
-    // 4 waves x 32 rows when 8-wave blocks would leave the chip less than half full.
-    // Otherwise 12 waves (three per SIMD: more of each wave's softmax runs under the other
+    // When 8-wave blocks would leave the chip less than half full: 8 waves over 128 rows with
+    // the keys split between two wave groups (two waves per SIMD on every CU, where plain
+    // 4-wave blocks would have one).  Otherwise 12 waves (three per SIMD: more of each wave's softmax runs under the other
     // waves' products, +3% on causal launches) when the blocks' work differs, i.e. the launch
     // walks several K/V blocks or the queries and keys share one positions array (a causal
     // triangle); the heavy blocks run first, so the last round of blocks is light.  Launches
@@ -595,9 +655,9 @@ hipError_t launch_block_fwd_bf16(const BlockFwdArgs& a, hipStream_t stream) {
     // part-filled last round of the 256 CUs (8% slower measured on such ring steps), while
     // 64-position blocks divide it evenly.
     const int64_t blocks8 = ((a.seq_q + 256 / p.G - 1) / (256 / p.G)) * p.n_cols;
-    if (blocks8 < 512) return launch_variant<4, 1, 2>(p, a.seq_q, stream);
-    if (a.n_blk > 1 || a.blk[0].pos == a.q_pos) return launch_variant<12, 1, 1>(p, a.seq_q, stream);
-    return launch_variant<8, 1, 2>(p, a.seq_q, stream);
+    if (blocks8 < 512) return launch_variant<8, 1, 2, 2>(p, a.seq_q, stream);
+    if (a.n_blk > 1 || a.blk[0].pos == a.q_pos) return launch_variant<12, 1, 1, 1>(p, a.seq_q, stream);
+    return launch_variant<8, 1, 2, 1>(p, a.seq_q, stream);
 }
 
 }  // namespace cpattn
