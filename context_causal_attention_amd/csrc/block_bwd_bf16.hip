@@ -171,14 +171,25 @@ __device__ inline TrOff tr_off(int lane, int db) {
 // ------------------------------------------------------------------------------------------
 // dq kernel
 // ------------------------------------------------------------------------------------------
-__global__ void __launch_bounds__(kThreads, 1) block_bwd_dq_kernel(const BwdParams p) {
+// KS = 1: 4 waves, each over both 32-key halves of every K/V tile.  KS = 2 (launches too small
+// to fill the chip): 8 waves, two per 32-row query group, one per 32-key half of every tile,
+// each with its own partial dQ; the second-half waves hand theirs over through LDS at the end.
+template <int KS>
+__global__ void __launch_bounds__(64 * kNW * KS, 1) block_bwd_dq_kernel(const BwdParams p) {
+    constexpr int NW = kNW * KS;
+    constexpr int kThr = 64 * NW;
+    constexpr int kRowsW = kTile / NW;  // tile rows each wave loads
+    constexpr int kLd = kRowsW / 4;
+    constexpr int NKB = 2 / KS;         // 32-key halves of a tile each wave takes
     __shared__ __attribute__((aligned(16))) char lds_stage0[2 * kTileBytes];  // [K|V]
     __shared__ __attribute__((aligned(16))) char lds_stage1[2 * kTileBytes];
-    __shared__ int red[2 * kNW];
+    __shared__ int red[2 * NW];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int w = tid >> 6;
+    const int w = KS > 1 ? __builtin_amdgcn_readfirstlane(tid >> 6) : (tid >> 6);
+    const int qg = KS > 1 ? w % kNW : w;     // query group: rows 32*qg .. +31 of the block
+    const int khalf = KS > 1 ? w / kNW : 0;  // with KS = 2: the 32-key half of each tile
     const int half = lane >> 5;
     const int l32 = lane & 31;
 
@@ -206,7 +217,7 @@ __global__ void __launch_bounds__(kThreads, 1) block_bwd_dq_kernel(const BwdPara
     // visible key tiles (a prefix) and tiles visible to every query of the block
     const int64_t n_tiles = (p.seq_kv + kTile - 1) / kTile;
     int c_ne = 0, c_full = 0;
-    for (int64_t t = tid; t < n_tiles; t += kThreads) {
+    for (int64_t t = tid; t < n_tiles; t += kThr) {
         c_ne += (p.kvpos[t * kTile] <= pmax) ? 1 : 0;
         const int64_t lk = t * kTile + kTile - 1;
         c_full += (lk < p.seq_kv && p.kvpos[lk] <= pmin) ? 1 : 0;
@@ -215,14 +226,14 @@ __global__ void __launch_bounds__(kThreads, 1) block_bwd_dq_kernel(const BwdPara
     c_full = wave_sum(c_full);
     if (lane == 0) {
         red[w] = c_ne;
-        red[kNW + w] = c_full;
+        red[NW + w] = c_full;
     }
     __syncthreads();
     int n_ne = 0, n_full = 0;
 #pragma unroll
-    for (int i = 0; i < kNW; ++i) {
+    for (int i = 0; i < NW; ++i) {
         n_ne += red[i];
-        n_full += red[kNW + i];
+        n_full += red[NW + i];
     }
 
     // K/V tile loads (both tensors row-read, same swizzle)
@@ -232,10 +243,10 @@ __global__ void __launch_bounds__(kThreads, 1) block_bwd_dq_kernel(const BwdPara
     const int64_t tile_bytes_g = (int64_t)kTile * kvstride * 2;
     const int ld_row_in = lane >> 4;
     const int ld_chunk = lane & 15;
-    uint32_t koff[kLoads];
+    uint32_t koff[kLd];
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-        const int row = w * kRowsPerWave + 4 * i + ld_row_in;
+    for (int i = 0; i < kLd; ++i) {
+        const int row = w * kRowsW + 4 * i + ld_row_in;
         koff[i] = (uint32_t)(row * kvstride * 2) + ((ld_chunk ^ swz(row)) << 4);
     }
     auto issue_tile = [&](int jt, LDS_AS char* kt) {
@@ -248,17 +259,17 @@ __global__ void __launch_bounds__(kThreads, 1) block_bwd_dq_kernel(const BwdPara
         const __amdgpu_buffer_rsrc_t kr = make_rsrc(kb_t, span);
         const __amdgpu_buffer_rsrc_t vr = make_rsrc(vb_t, span);
 #pragma unroll
-        for (int i = 0; i < kLoads; ++i) {
-            const int row = w * kRowsPerWave + 4 * i + ld_row_in;
+        for (int i = 0; i < kLd; ++i) {
+            const int row = w * kRowsW + 4 * i + ld_row_in;
             // rows past the end re-read the last key (finite data the mask hides)
             const uint32_t back = (row > rmax) ? (uint32_t)((row - rmax) * kvstride * 2) : 0u;
-            load_lds16(kr, koff[i] - back, kt + (w * kRowsPerWave + 4 * i) * kRowBytes);
-            load_lds16(vr, koff[i] - back, vt + (w * kRowsPerWave + 4 * i) * kRowBytes);
+            load_lds16(kr, koff[i] - back, kt + (w * kRowsW + 4 * i) * kRowBytes);
+            load_lds16(vr, koff[i] - back, vt + (w * kRowsW + 4 * i) * kRowBytes);
         }
     };
 
     // this lane's query row: q and dout as B operands, lse (log2 domain) and D as scalars
-    const int row0 = w * 32;
+    const int row0 = qg * 32;
     const int hs = row0 / p.pq;
     const int64_t i = q0 + (row0 % p.pq) + l32;
     const int64_t head = (int64_t)kvh * p.ratio + (int64_t)hg * p.G + hs;
@@ -306,50 +317,54 @@ __global__ void __launch_bounds__(kThreads, 1) block_bwd_dq_kernel(const BwdPara
         const LDS_AS char* vt = kt + kTileBytes;
         if (jt + 1 < n_ne) issue_tile(jt + 1, nxt);
 
-        // S^T = K Q^T and dP^T = V dO^T for the tile's two 32-key blocks
-        f32x16 s[2], dp[2];
+        // S^T = K Q^T and dP^T = V dO^T for this wave's 32-key blocks of the tile (key block
+        // kb = khalf * NKB + kk)
+        f32x16 s[NKB], dp[NKB];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            s[kb] = f32x16{};
-            dp[kb] = f32x16{};
+        for (int kk = 0; kk < NKB; ++kk) {
+            s[kk] = f32x16{};
+            dp[kk] = f32x16{};
         }
 #pragma unroll
         for (int ks = 0; ks < kD / 16; ++ks)
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+            for (int kk = 0; kk < NKB; ++kk) {
+                const int kb = khalf * NKB + kk;
                 const bf16x8 ka = lds_b128(kt + kb * 32 * kRowBytes + off_r[ks]);
                 const bf16x8 va = lds_b128(vt + kb * 32 * kRowBytes + off_r[ks]);
-                s[kb] = mfma(ka, qreg[ks], s[kb]);
-                dp[kb] = mfma(va, doreg[ks], dp[kb]);
+                s[kk] = mfma(ka, qreg[ks], s[kk]);
+                dp[kk] = mfma(va, doreg[ks], dp[kk]);
             }
-        sched_reads_ahead<16, 2, 2, 1>();
+        sched_reads_ahead<8 * NKB, 2, 2, 1>();
 
         // ds = p (dp - D); entry v of key block kb is key 32*kb + 8*(v/4) + 4*half + v%4
         const bool masked = jt >= n_full;
         const int64_t rel = vis - (int64_t)jt * kTile - 4 * half;
         const int lim = rel < 0 ? 0 : (rel > kTile ? kTile : (int)rel);
-        bf16x8 dsb[2][2];
+        bf16x8 dsb[NKB][2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kk = 0; kk < NKB; ++kk)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][v], p.c, -lse2));
+                const int kb = khalf * NKB + kk;
+                float pv = __builtin_amdgcn_exp2f(fmaf(s[kk][v], p.c, -lse2));
                 if (masked && 32 * kb + 8 * (v / 4) + v % 4 >= lim) pv = 0.f;
-                dsb[kb][v >> 3][v & 7] = (__bf16)(pv * (dp[kb][v] - dlt));
+                dsb[kk][v >> 3][v & 7] = (__bf16)(pv * (dp[kk][v] - dlt));
             }
 
         // dQ^T += K^T dS^T
 #pragma unroll
         for (int db = 0; db < kD / 32; ++db)
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int kk = 0; kk < NKB; ++kk)
 #pragma unroll
                 for (int ks2 = 0; ks2 < 2; ++ks2) {
+                    const int kb = khalf * NKB + kk;
                     const LDS_AS char* base = kt + (32 * kb + 16 * ks2) * kRowBytes;
                     const bf16x8 a = lds_tr_pair(base + off_t[db].a, base + off_t[db].b);
-                    acc[db] = mfma(a, dsb[kb][ks2], acc[db]);
+                    acc[db] = mfma(a, dsb[kk][ks2], acc[db]);
                 }
-        sched_reads_ahead<16, 1, 2, 2>();
+        sched_reads_ahead<8 * NKB, 1, 2, 2>();
 
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next tile has landed
         __syncthreads();
@@ -363,6 +378,23 @@ __global__ void __launch_bounds__(kThreads, 1) block_bwd_dq_kernel(const BwdPara
         if (jt + 1 < n_ne) tile(jt + 1, st1, st0);
     }
 
+    if constexpr (KS > 1) {
+        // the key halves' partial sums meet in the first-half waves (each stage holds two
+        // waves' 16 KB; the stages are free after the loop)
+        LDS_AS float* xch = (LDS_AS float*)((qg >> 1) ? lds_stage1 : lds_stage0) + (qg & 1) * (64 * 64);
+        if (khalf == 1) {
+#pragma unroll
+            for (int db = 0; db < kD / 32; ++db)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) xch[(db * 16 + v) * 64 + lane] = acc[db][v];
+        }
+        __syncthreads();
+        if (khalf != 0) return;
+#pragma unroll
+        for (int db = 0; db < kD / 32; ++db)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[db][v] += xch[(db * 16 + v) * 64 + lane];
+    }
     // dq += scale * dQ; accumulator entry v of block db is dimension 32*db + 8*(v/4) + 4*half + v%4
     if (!valid) return;
     float* drow = p.dq + qrow * kD;
@@ -702,7 +734,11 @@ hipError_t launch_block_bwd_bf16(const BlockBwdArgs& a, hipStream_t stream) {
     p.kv_xcd_cols = (p.kv_cols % 8 == 0) ? p.kv_cols / 8 : 0;
     p.write_dq = a.write_dq ? 1 : 0;
     p.write_dkv = a.write_dkv ? 1 : 0;
-    hipLaunchKernelGGL(block_bwd_dq_kernel, dim3((unsigned)(p.n_qt * p.n_cols)), dim3(kThreads), 0, stream, p);
+    // launches of fewer than two blocks per CU split each tile's keys over two wave groups
+    if (p.n_qt * p.n_cols < 512)
+        hipLaunchKernelGGL(block_bwd_dq_kernel<2>, dim3((unsigned)(p.n_qt * p.n_cols)), dim3(2 * kThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL(block_bwd_dq_kernel<1>, dim3((unsigned)(p.n_qt * p.n_cols)), dim3(kThreads), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(block_bwd_dkdv_kernel, dim3((unsigned)(p.n_kb * p.kv_cols)), dim3(kThreadsKv), 0, stream, p);
