@@ -45,6 +45,22 @@ def test_fused_ring_share_equals_tile_then_merge(dtype, C, t, Hq, Hkv, B):
         assert _same_bits(fo, uo) and _same_bits(fl, ul), f"rank {r}"
 
 
+def test_fused_ring_share_equals_tile_then_merge_at_launch_size():
+    """The same at launch sizes (6000 local rows, 32/8 heads): the diagonal step shares the
+    query positions tensor (12-wave kernel), the other steps do not (8-wave kernel)."""
+    C, t, Hq, Hkv, B, D = 4, 3000, 32, 8, 1, 128
+    S = 2 * C * t
+    pos = [cp.zigzag_index(S, C, o, device=DEV) for o in range(C)]
+    ks = [_rand(400 + o, (B, 2 * t, Hkv, D), "bf16").to(DEV) for o in range(C)]
+    vs = [_rand(500 + o, (B, 2 * t, Hkv, D), "bf16").to(DEV) for o in range(C)]
+    for r in (0, 2):
+        q = _rand(600 + r, (B, 2 * t, Hq, D), "bf16").to(DEV)
+        fo, fl = cp.ring_share_fwd(q, ks, vs, pos, r, 1 / math.sqrt(D), mode="fused")
+        uo, ul = cp.ring_share_fwd(q, ks, vs, pos, r, 1 / math.sqrt(D), mode="unfused")
+        torch.cuda.synchronize()
+        assert _same_bits(fo, uo) and _same_bits(fl, ul), f"rank {r}"
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_two_key_halves_merge_to_full_attention(dtype):
     """Keys split at an arbitrary point: block_fwd over the first part, block_fwd_merge over
