@@ -32,12 +32,13 @@ HIP_FLAGS = [
 ]
 
 
-# Per-file flags.  Kernels allowed more than 256 registers per lane (one wave per SIMD: the
-# backward kernels and the forward's 4-wave variant) otherwise get accumulator-register (AGPR)
-# destinations for their matrix products, and every score is copied out of them for the
-# vector math (v_accvgpr_read/write around each product).  The vector-register form keeps the
-# products' results where the vector instructions read them; AGPRs then serve only as spill
-# space.  (The forward's 8-wave variant compiles to the same code either way.)
+# Per-file flags.  Kernels allowed more than 256 registers per lane (one wave per SIMD, as the
+# backward's 4-wave dq kernel) otherwise get accumulator-register (AGPR) destinations for
+# their matrix products, and every score is copied out of them for the vector math
+# (v_accvgpr_read/write around each product).  The vector-register form keeps the products'
+# results where the vector instructions read them; AGPRs then serve only as spill space.
+# (Kernels with two or three waves per SIMD, as every forward variant, compile to the same
+# code either way.)
 _VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]
 FILE_FLAGS = {
     "block_bwd_bf16.hip": _VGPR_FORM,

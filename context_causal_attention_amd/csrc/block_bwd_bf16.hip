@@ -17,6 +17,8 @@
 // of 64 keys are staged in LDS (direct global->LDS loads, two stages).  Per tile:
 //   S^T = K Q^T and dP^T = V dO^T (K, V rows read from LDS), p and ds per lane (one query:
 //   lse and D are per-lane scalars), dQ^T += K^T dS^T (K read transposed, ds_read_b64_tr_b16).
+//   Launches too small to fill the chip take 8 waves instead, two per 32-row query group, each
+//   over one 32-key half of every tile (block_bwd_dq_kernel<2>).
 // dk/dv kernel: a block of 8 waves owns 128 keys of one K/V head, in 4 groups of 32 (one key
 // per lane; k as a matrix operand in registers, the block's v rows in LDS), and walks the
 // query tiles of 64 rows that see them, for every query head of the group.  Q, dO, lse and D
