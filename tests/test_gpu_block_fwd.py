@@ -189,3 +189,52 @@ def test_large_zigzag_steps_and_share():
     out, lse = cp.ring_share_fwd(q, ks, vs, tpos, r, scale)
     torch.cuda.synchronize()
     _check_rows(out, lse, rows, ref_o, ref_l, "one-launch share")
+
+
+def _random_case(seed: int):
+    """A seeded shape: batch, sizes, head ratio, positions (contiguous causal, a shared
+    positions tensor, or sparse increasing sets), small or at launch size."""
+    rng = np.random.default_rng(seed)
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    ratio = int(rng.choice([1, 2, 3, 4, 8]))
+    hq = hkv * ratio
+    B = int(rng.integers(1, 3))
+    large = bool(rng.integers(0, 2))
+    # at launch size the 8-wave blocks (256/G positions of G query heads) number >= 512
+    G = 4 if ratio % 4 == 0 else (2 if ratio % 2 == 0 else 1)
+    cols = B * hkv * (ratio // G)
+    if large:
+        sq = max(1, -(-520 // cols) * (256 // G) + int(rng.integers(-90, 90)))
+    else:
+        sq = int(rng.integers(1, 700))
+    kind = str(rng.choice(["shared", "causal", "sparse"]))
+    if kind == "sparse":
+        skv = int(rng.integers(1, 2 * sq + 2))
+        qpos = np.sort(rng.choice(4 * (sq + skv), sq, replace=False)).astype(np.int64)
+        kvpos = np.sort(rng.choice(4 * (sq + skv), skv, replace=False)).astype(np.int64)
+    else:
+        skv = sq if kind == "shared" else sq + int(rng.integers(0, 300))
+        kvpos = np.arange(skv, dtype=np.int64)
+        qpos = kvpos[skv - sq:].copy()
+    return B, sq, skv, hq, hkv, kind, qpos, kvpos
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_shapes_sampled(seed):
+    """Seeded random shapes through whichever kernel the launcher picks; sampled rows (every
+    row when small) against the oracle, and empty rows exactly (0, -inf)."""
+    B, sq, skv, hq, hkv, kind, qpos, kvpos = _random_case(seed)
+    D, scale = 128, 1 / math.sqrt(128)
+    q, k, v = _inputs(7000 + seed, B, sq, skv, hq, hkv, D, torch.bfloat16)
+    rows = _rows(sq, seed) if sq > 700 else np.arange(sq, dtype=np.int64)
+    ref_o, ref_l = oracle.attention_rows(q.float().numpy(), k.float().numpy(), v.float().numpy(), qpos, kvpos,
+                                         scale, rows=rows)
+    tq = torch.from_numpy(qpos).to(DEV)
+    tk = tq if kind == "shared" else torch.from_numpy(kvpos).to(DEV)
+    out, lse = cp.block_fwd(q.to(DEV), k.to(DEV), v.to(DEV), tq, tk, scale)
+    torch.cuda.synchronize()
+    _check_rows(out, lse, rows, ref_o, ref_l, f"seed {seed}: B={B} Sq={sq} Skv={skv} Hq={hq} Hkv={hkv} {kind}")
+    lv = lse[:, :, rows].cpu().numpy()
+    empty = np.isneginf(ref_l)
+    assert np.array_equal(np.isneginf(lv), empty)
+    assert np.all(out[:, rows].cpu().numpy().transpose(0, 2, 1, 3)[empty] == 0.0)
