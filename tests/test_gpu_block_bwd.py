@@ -1,8 +1,10 @@
 """HIP attention backward against the oracle: the row term D, the block backward (both
-dtypes, GQA, every zigzag step class, sparse positions with empty rows, ragged tails), the
-write/accumulate flags, and the ring-share backward at the 8K and 256K workloads (sampled rows
-and keys, in the launch sequence the benchmark times; at 256K the saved forward state is
-synthetic, since the oracle cannot run that forward for every row).
+dtypes, GQA, every zigzag step class, sparse positions with empty rows, ragged tails; small
+launches run the dq kernel with its keys split over two wave groups), the write/accumulate
+flags, launch-size blocks with ragged ends (the 4-wave dq kernel), and the ring-share backward
+at the 8K and 256K workloads (sampled rows and keys, in the launch sequence the benchmark
+times; at launch size the saved forward state is synthetic, since the oracle cannot run that
+forward for every row).
 
 Tolerances: fp32, 1e-5 times max(1, largest reference magnitude).  bf16: p and ds are
 rounded to bf16 (relative error <= 2^-9 each) before the products that use them; on these
@@ -209,3 +211,43 @@ def test_ring_share_bwd_8k():
 
 def test_ring_share_bwd_256k_sampled():
     _ring_bwd_check(WORKLOADS["ring_share_256k"], rows_per_chunk=2, key_samples=4, exact_forward=False)
+
+
+@pytest.mark.parametrize("B,S,Hq,Hkv", [(1, 9000, 32, 8), (2, 5000, 16, 8)])
+def test_block_bwd_launch_size_sampled(B, S, Hq, Hkv):
+    """Causal self-attention backward at launch size (the 4-wave dq kernel, at least 512
+    blocks; ragged last tiles), from a synthetic saved state (seeded out; an upper bound of
+    each row's lse, so every weight stays below 1).  Sampled dq rows and dk, dv keys against
+    the oracle."""
+    D = 128
+    scale = 1 / math.sqrt(D)
+    q, k, v, g = (_rand(S + i, s, "bf16") for i, s in
+                  enumerate(((B, S, Hq, D), (B, S, Hkv, D), (B, S, Hkv, D), (B, S, Hq, D))))
+    qf, kf, vf, gf = (x.float().numpy() for x in (q, k, v, g))
+    pos = np.arange(S, dtype=np.int64)
+    out = torch.randn((B, S, Hq, D), generator=torch.Generator().manual_seed(78)).numpy().astype(np.float32)
+    kmax = float(np.sqrt((kf.astype(np.float64) ** 2).sum(-1)).max())
+    qn = np.sqrt((qf.astype(np.float64) ** 2).sum(-1))  # [B, S, Hq]
+    lse = np.ascontiguousarray((scale * qn * kmax + np.log(pos + 1.0)[None, :, None]).transpose(0, 2, 1),
+                               dtype=np.float32)
+    tp = torch.from_numpy(pos).to(DEV)
+    o_t, l_t = torch.from_numpy(out).to(DEV), torch.from_numpy(lse).to(DEV)
+    gd = g.to(DEV)
+    delta = cp.attn_bwd_delta(o_t, gd)
+    dq = torch.empty((B, S, Hq, D), device=DEV)
+    dk = torch.empty((B, S, Hkv, D), device=DEV)
+    dv = torch.empty((B, S, Hkv, D), device=DEV)
+    cp.block_bwd(q.to(DEV), k.to(DEV), v.to(DEV), gd, tp, tp, scale, l_t, delta, dq, dk, dv,
+                 cp.BWD_WRITE_DQ | cp.BWD_WRITE_DKV)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(S)
+    edges = [0, 1, 31, 32, 63, 64, 127, 128, S - 65, S - 64, S - 33, S - 2, S - 1]
+    rows = np.unique(np.concatenate([edges, rng.integers(0, S, 12)])).astype(np.int64)
+    ref_dq, _, _ = oracle.block_bwd(qf, kf, vf, gf, out, lse, pos, pos, scale, qrows=rows,
+                                    krows=np.zeros(0, dtype=np.int64))
+    _check("dq", dq[:, torch.from_numpy(rows).to(DEV)], ref_dq, "bf16")
+    _, rdk, rdv = oracle.block_bwd(qf, kf, vf, gf, out, lse, pos, pos, scale,
+                                   qrows=np.zeros(0, dtype=np.int64), krows=rows)
+    kidx = torch.from_numpy(rows).to(DEV)
+    _check("dk", dk[:, kidx], rdk, "bf16")
+    _check("dv", dv[:, kidx], rdv, "bf16")
