@@ -374,12 +374,17 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
     // one tile: prefetch the next tile into `nxt`, compute the current one from `cur`
     auto tile = [&](const LDS_AS char* kt, LDS_AS char* nxt) {
         const LDS_AS char* vt = kt + kTileBytes;
-        if (on < p.n_blk) issue_tile(on, jn, nxt);
+        // The next tile's loads go out at the start of the tile, or, in the two-pass variant,
+        // between the passes: right after the barrier all twelve waves start their score
+        // products at once, and issuing the loads there too slowed the kernel (between the
+        // passes: +2-4%, the loads still land within the second pass).
+        if (KBP != 1 && on < p.n_blk) issue_tile(on, jn, nxt);
 
         // the tile in 2 / KBP passes of 32 * KBP keys each: scores, mask, softmax, PV (with the
         // keys split, a group whose share has run out only keeps the barriers)
 #pragma unroll
         for (int ps = 0; ps < ((KS == 1 || oc < p.n_blk) ? 2 / KBP : 0); ++ps) {
+            if (KBP == 1 && ps == 1 && on < p.n_blk) issue_tile(on, jn, nxt);
             // S^T = K Q^T
             f32x16 s[NB][KBP];
 #pragma unroll
