@@ -8,8 +8,8 @@
 //   kv_pos[j] <= q_pos[i]:  out_i = softmax_j(scale <q_i, k_j>) v_j,  lse_i = ln sum_j e^(s_ij).
 //
 // Work decomposition.  A block of NW waves owns G query heads that share one K/V head
-// (G = 4, 2 or 1, whichever divides heads_q/heads_kv) times PQ = 32*NW*NB/G query
-// positions.  Each wave owns NB column blocks of 32 query rows; every lane holds one query
+// (G = 4, 2 or 1, whichever divides heads_q/heads_kv) times PQ = 32*(NW/KS)*NB/G query
+// positions (KS: the key split below, else 1).  Each wave owns NB column blocks of 32 query rows; every lane holds one query
 // row of each column block.  With NW = 8 two waves share a SIMD, so one wave's matrix
 // products overlap the other's softmax; with NW = 12, three.  At three waves per SIMD a wave
 // has 168 registers, too few for a whole tile's scores and weights, so that variant takes
@@ -41,7 +41,7 @@
 // K and V tiles go from global memory straight into LDS (buffer_load_dwordx4 ... lds; each
 // lane lands 16 bytes at base + 16*lane, so the XOR-swizzled layout is chosen by which chunk
 // each lane fetches).  Two LDS stages: the next tile is in flight while the current one is
-// used.  Buffer loads rather than global_load_lds: the compiler treats a pending global LDS
+// used (issued at the start of the tile, or between the passes in the two-pass variant).  Buffer loads rather than global_load_lds: the compiler treats a pending global LDS
 // load as a flat access and then waits for every outstanding LDS read (lgkmcnt(0)) before
 // each product, instead of only for the read the product needs.
 //
@@ -651,13 +651,13 @@ hipError_t launch_block_fwd_bf16(const BlockFwdArgs& a, hipStream_t stream) {
     p.merge = a.merge ? 1 : 0;
     // When 8-wave blocks would leave the chip less than half full: 8 waves over 128 rows with
     // the keys split between two wave groups (two waves per SIMD on every CU, where plain
-    // 4-wave blocks would have one).  Otherwise 12 waves (three per SIMD: more of each wave's softmax runs under the other
-    // waves' products, +3% on causal launches) when the blocks' work differs, i.e. the launch
-    // walks several K/V blocks or the queries and keys share one positions array (a causal
-    // triangle); the heavy blocks run first, so the last round of blocks is light.  Launches
-    // of equal-work blocks (queries against another shard's keys) keep 8 waves: 12-wave
-    // blocks hold 384/G positions (96 for G = 4), which split a power-of-two shard into a
-    // part-filled last round of the 256 CUs (8% slower measured on such ring steps), while
+    // 4-wave blocks would have one).  Otherwise 12 waves (three per SIMD: more of each wave's
+    // softmax runs under the other waves' products; +5-7% on causal launches) when the
+    // blocks' work differs, i.e. the launch walks several K/V blocks or the queries and keys
+    // share one positions array (a causal triangle): the heavy blocks run first, so the last
+    // round of blocks is light.  Launches of equal-work blocks (queries against another
+    // shard's keys) keep 8 waves: 12-wave blocks hold 384/G positions (96 for G = 4), which
+    // split a power-of-two shard into a part-filled last round of the 256 CUs, while
     // 64-position blocks divide it evenly.
     const int64_t blocks8 = ((a.seq_q + 256 / p.G - 1) / (256 / p.G)) * p.n_cols;
     if (blocks8 < 512) return launch_variant<8, 1, 2, 2>(p, a.seq_q, stream);
