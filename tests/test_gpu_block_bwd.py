@@ -251,3 +251,26 @@ def test_block_bwd_launch_size_sampled(B, S, Hq, Hkv):
     kidx = torch.from_numpy(rows).to(DEV)
     _check("dk", dk[:, kidx], rdk, "bf16")
     _check("dv", dv[:, kidx], rdv, "bf16")
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_block_bwd_random_shapes(seed):
+    """Seeded random small shapes (batch 1-2, K/V heads 1-4, head ratios 1-4, causal or sparse
+    increasing positions, ragged sizes), both dtypes: every dq, dk, dv entry against the
+    oracle, from the oracle's own forward."""
+    rng = np.random.default_rng(100 + seed)
+    B = int(rng.integers(1, 3))
+    hkv = int(rng.choice([1, 2, 4]))
+    hq = hkv * int(rng.choice([1, 2, 3, 4]))
+    sq, skv = int(rng.integers(1, 260)), int(rng.integers(1, 330))
+    if rng.integers(0, 2):
+        qpos = np.sort(rng.choice(3 * (sq + skv), sq, replace=False)).astype(np.int64)
+        kvpos = np.sort(rng.choice(3 * (sq + skv), skv, replace=False)).astype(np.int64)
+    else:
+        n = max(sq, skv)
+        kvpos = np.arange(n - skv, n, dtype=np.int64)
+        qpos = np.arange(n - sq, n, dtype=np.int64)
+    for dtype in ("bf16", "fp32"):
+        got, ref, _ = _block_case(200 + seed, B, sq, skv, hq, hkv, 128, dtype, qpos, kvpos)
+        for name, x, r in zip(("dq", "dk", "dv"), got, ref):
+            _check(f"seed {seed} {dtype} B={B} Sq={sq} Skv={skv} Hq={hq} Hkv={hkv} {name}", x, r, dtype)
