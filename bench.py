@@ -58,7 +58,10 @@ def parse_args(argv=None):
                          "step) instead of the forward; ring_share workloads only")
     ap.add_argument("--mode", choices=("single", "fused", "unfused"), default="single",
                     help="ring share: one launch over all ring blocks (single), one launch per step "
-                         "merging in its epilogue (fused), or per-step tiles plus the merge kernel")
+                         "merging in its epilogue (fused), or per-step tiles plus the merge kernel "
+                         "(unfused); Ulysses with one batch and contiguous shards: unfused runs the "
+                         "exchanges as separate permute kernels instead of the attention's row "
+                         "addressing")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--no-sclk", action="store_true",
@@ -145,6 +148,15 @@ class Plan:
             self.lg = torch.empty((w.batch, hq, w.seq_len), dtype=torch.float32, device=dev)
             self.ost = torch.zeros((C, w.batch, s, w.heads_q, w.head_dim), dtype=torch.float32, device=dev)
             S = w.seq_len
+            # one batch, contiguous shards: global row i of the group is row i of the stacked
+            # buffers at the group's head offset, so the attention reads and writes them in place
+            self.rows = mode != "unfused" and w.batch == 1 and not w.zigzag and td == torch.bfloat16
+            if self.rows:
+                Hq, Hk = w.heads_q, w.heads_kv
+                self.qrows = self.qst.view(S, Hq, w.head_dim)[:, g * hq:(g + 1) * hq]
+                self.krows = self.kst.view(S, Hk, w.head_dim)[:, g * hk:(g + 1) * hk]
+                self.vrows = self.vst.view(S, Hk, w.head_dim)[:, g * hk:(g + 1) * hk]
+                self.orows = self.ost.view(S, Hq, w.head_dim)[:, g * hq:(g + 1) * hq]
             self.attn_flops.append(4.0 * w.batch * hq * w.head_dim * (S * (S + 1) // 2))
         elif w.kind == "usp":
             A = w.a2a
@@ -249,6 +261,9 @@ class Plan:
             for rr in range(C):
                 cp.zigzag_index(w.seq_len, C, rr, out=self.pos[rr])
                 attn(self.qs[rr], self.kseq, self.vseq, self.pos[rr], self.gpos, w.scale, self.out, self.lse)
+        elif self.kind == "ulysses" and self.rows:
+            attn(self.qrows, self.krows, self.vrows, self.gpos, self.gpos, w.scale, self.orows, self.lg,
+                 fn=cp.block_fwd_rows)
         elif self.kind == "ulysses":
             g, zz = w.group, w.zigzag
             nb = lambda x: 2 * x.numel() * x.element_size()  # noqa: E731  (read + write)
@@ -582,7 +597,7 @@ def main(argv=None) -> int:
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic (seeded iid N(0,1), per-chunk generators)",
-        "config": {"workload": w.name + (f"_{args.mode}" if args.mode != "single" and w.kind == "ring_share" else "")
+        "config": {"workload": w.name + (f"_{args.mode}" if args.mode != "single" and w.kind in ("ring_share", "ulysses") else "")
                    + ("_bwd" if bwd else "") + ("_graph" if graph is not None else ""),
                    "batch": w.batch, "a2a": w.a2a, "zigzag": w.zigzag, "seq_len": w.seq_len, "cp_size": w.cp_size,
                    "rank": w.rank, "group": w.group, "heads_q": w.heads_q, "heads_kv": w.heads_kv,

@@ -17,6 +17,7 @@ from ._binding import (  # noqa: F401
     block_bwd,
     block_fwd,
     block_fwd_merge,
+    block_fwd_rows,
     header_entry_points,
     library_path,
     load_library,

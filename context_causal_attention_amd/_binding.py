@@ -55,6 +55,7 @@ def load_library():
     L.cpattn_zigzag_index.argtypes = [i64, i32, i32, P, P]
     L.cpattn_block_fwd.argtypes = [P, P, P, ctypes.c_int, i32, i64, i64, i32, i32, i32, P, P, f32, P, P, P]
     L.cpattn_block_fwd_merge.argtypes = list(L.cpattn_block_fwd.argtypes)
+    L.cpattn_block_fwd_rows.argtypes = [P, i64, P, P, i64, i64, i64, i32, i32, i32, P, P, f32, P, i64, P, P]
     L.cpattn_lse_merge.argtypes = [P, P, P, P, i32, i64, i32, i32, P]
     L.cpattn_ring_share_fwd.argtypes = [P, P, P, P, P, i32, ctypes.c_int, i32, i64, i32, i32, i32, P, f32, P, P, P]
     L.cpattn_attn_bwd_delta.argtypes = [P, P, ctypes.c_int, i32, i64, i32, i32, P, P]
@@ -63,7 +64,8 @@ def load_library():
     L.cpattn_reorder_gathered.argtypes = [P, P, i32, i64, i64, i32, ctypes.c_int, P]
     L.cpattn_ulysses_permute.argtypes = [P, P, i32, i32, i64, i32, i32, i32, i32, ctypes.c_int, P]
     L.cpattn_ulysses_permute_zigzag.argtypes = list(L.cpattn_ulysses_permute.argtypes)
-    for name in ("cpattn_zigzag_index", "cpattn_block_fwd", "cpattn_block_fwd_merge", "cpattn_lse_merge",
+    for name in ("cpattn_zigzag_index", "cpattn_block_fwd", "cpattn_block_fwd_merge", "cpattn_block_fwd_rows",
+                 "cpattn_lse_merge",
                  "cpattn_attn_bwd_delta", "cpattn_block_bwd", "cpattn_ring_share_fwd",
                  "cpattn_reorder_gathered", "cpattn_ulysses_permute", "cpattn_ulysses_permute_zigzag"):
         getattr(L, name).restype = ctypes.c_int
@@ -148,6 +150,49 @@ def block_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_pos: torch.Te
     Returns (out fp32 [B, Sq, Hq, D], lse fp32 [B, Hq, Sq]).
     """
     return _block_fwd_call("cpattn_block_fwd", q, k, v, q_pos, kv_pos, scale, out, lse, alloc=True)
+
+
+def _rows_view(t: torch.Tensor, name: str, dtype, heads: int | None = None):
+    """A [rows, heads, D] view whose rows may be strided; heads and head dims dense."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if t.dtype != dtype or t.dim() != 3:
+        raise ValueError(f"{name} must be a 3-d {dtype} view [rows, heads, head_dim]")
+    if heads is not None and t.shape[1] != heads:
+        raise ValueError(f"{name} must have {heads} heads (got {t.shape[1]})")
+    if t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+        raise ValueError(f"{name}: heads and head dims must be dense within a row")
+    return t.stride(0)
+
+
+def block_fwd_rows(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_pos: torch.Tensor,
+                   kv_pos: torch.Tensor, scale: float, out: torch.Tensor, lse: torch.Tensor | None = None):
+    """cpattn_block_fwd_rows: bf16 block attention (batch 1) on row views.
+
+    q [Sq, Hq, 128], k, v [Skv, Hkv, 128] (bf16) and out [Sq, Hq, 128] (fp32) are views whose
+    rows (dim 0) may be strided, e.g. one head group of a stacked buffer; within a row the
+    heads and head dims are dense.  Writes out in place; returns (out, lse [1, Hq, Sq]).
+    """
+    L = load_library()
+    Sq, Hq, D = q.shape
+    Skv, Hkv = k.shape[0], k.shape[1]
+    qs = _rows_view(q, "q", torch.bfloat16)
+    ks = _rows_view(k, "k", torch.bfloat16)
+    if _rows_view(v, "v", torch.bfloat16, Hkv) != ks or v.shape[0] != Skv:
+        raise ValueError("v must have k's shape and row stride")
+    os_ = _rows_view(out, "out", torch.float32, Hq)
+    if out.shape[0] != Sq:
+        raise ValueError("out must have q's rows")
+    _need(q_pos, "q_pos", torch.int64, (Sq,))
+    _need(kv_pos, "kv_pos", torch.int64, (Skv,))
+    if lse is None:
+        lse = torch.empty((1, Hq, Sq), dtype=torch.float32, device=q.device)
+    _need(lse, "lse", torch.float32, (1, Hq, Sq))
+    _check(L.cpattn_block_fwd_rows(_ptr(q), qs, _ptr(k), _ptr(v), ks, Sq, Skv, Hq, Hkv, D, _ptr(q_pos),
+                                   _ptr(kv_pos), float(scale), _ptr(out), os_, _ptr(lse), _stream(q.device)))
+    return out, lse
 
 
 def block_fwd_merge(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_pos: torch.Tensor,
@@ -298,15 +343,34 @@ def ring_share_fwd(q: torch.Tensor, k_blocks, v_blocks, positions, rank: int, sc
 
 
 def ulysses_share_fwd(q_st: torch.Tensor, k_st: torch.Tensor, v_st: torch.Tensor, group: int,
-                      scale: float, out_st: torch.Tensor, zigzag: bool = True):
+                      scale: float, out_st: torch.Tensor, zigzag: bool = True, fused: bool | None = None):
     """Head group ``group``'s share of Ulysses attention from the stacked rank shards
     [C, B, S/C, H, D] of Q, K and V ("On Context Parallelism", All-to-all): the
     sequence-to-heads exchange (zigzag shards: with the chunk reorder folded in), causal
     attention over the whole sequence on global positions, and the inverse exchange of the
     output into the group's heads of ``out_st`` (fp32 [C, B, S/C, Hq, D]).
-    Returns (out_grouped [B, S, Hq/C, D], lse [B, Hq/C, S])."""
-    C, B, s, _, _ = q_st.shape
+    Returns (out_grouped [B, S, Hq/C, D], lse [B, Hq/C, S]).
+
+    ``fused`` (default: whenever possible, i.e. B = 1, contiguous shards, bf16, D = 128): with
+    one batch and contiguous shards, global row i of the group is row i of the stacked buffer
+    at the group's head offset, so the attention reads Q, K, V in place and writes out_st
+    directly (cpattn_block_fwd_rows), with the same bits as the explicit exchanges; out_grouped
+    is then a view into out_st."""
+    C, B, s, Hq, D = q_st.shape
     S = s * C
+    if fused is None:
+        fused = (B == 1 and not zigzag and q_st.dtype == torch.bfloat16 and D == 128
+                 and all(t.is_contiguous() for t in (q_st, k_st, v_st, out_st)))
+    if fused:
+        Hkv = k_st.shape[3]
+        hq, hk = Hq // C, Hkv // C
+        qv = q_st.view(S, Hq, D)[:, group * hq:(group + 1) * hq]
+        kv = k_st.view(S, Hkv, D)[:, group * hk:(group + 1) * hk]
+        vv = v_st.view(S, Hkv, D)[:, group * hk:(group + 1) * hk]
+        ov = out_st.view(S, Hq, D)[:, group * hq:(group + 1) * hq]
+        pos = zigzag_index(S, 1, 0, device=q_st.device)  # 0 .. S-1: global order
+        _, lse = block_fwd_rows(qv, kv, vv, pos, pos, scale, ov)
+        return ov.unsqueeze(0), lse
     qg = ulysses_seq_to_heads(q_st, group, zigzag=zigzag)
     kg = ulysses_seq_to_heads(k_st, group, zigzag=zigzag)
     vg = ulysses_seq_to_heads(v_st, group, zigzag=zigzag)

@@ -141,6 +141,47 @@ CPATTN_API cpattn_status_t cpattn_block_fwd_merge(const void* q, const void* k, 
                             heads_kv, head_dim, q_positions, kv_positions, scale, out, lse, stream);
 }
 
+CPATTN_API cpattn_status_t cpattn_block_fwd_rows(const void* q, int64_t q_row_stride, const void* k,
+                                                 const void* v, int64_t kv_row_stride, int64_t seq_q,
+                                                 int64_t seq_kv, int32_t heads_q, int32_t heads_kv,
+                                                 int32_t head_dim, const int64_t* q_positions,
+                                                 const int64_t* kv_positions, float scale, float* out,
+                                                 int64_t out_row_stride, float* lse, void* stream) {
+    const char* name = "block_fwd_rows";
+    if (heads_q <= 0 || heads_kv <= 0) return fail(CPATTN_ERR_INVALID_ARG, "%s: head counts must be > 0", name);
+    if (seq_q < 0 || seq_kv < 0) return fail(CPATTN_ERR_INVALID_ARG, "%s: sequence lengths must be >= 0", name);
+    if (!(scale > 0.f) || !isfinite(scale))
+        return fail(CPATTN_ERR_INVALID_ARG, "%s: scale must be finite and > 0", name);
+    if (heads_q % heads_kv != 0)
+        return fail(CPATTN_ERR_SHAPE, "%s: heads_q %d not a multiple of heads_kv %d", name, heads_q, heads_kv);
+    if (head_dim != 128) return fail(CPATTN_ERR_UNSUPPORTED, "%s: head_dim %d (supported: 128)", name, head_dim);
+    const int64_t qw = (int64_t)heads_q * head_dim, kw = (int64_t)heads_kv * head_dim;
+    if (q_row_stride < qw || q_row_stride % 8 != 0 || q_row_stride > (1LL << 24) || kv_row_stride < kw ||
+        kv_row_stride % 8 != 0 || kv_row_stride > (1LL << 24) || out_row_stride < qw || out_row_stride % 4 != 0)
+        return fail(CPATTN_ERR_UNSUPPORTED,
+                    "%s: row strides must cover the row (q %lld, kv %lld, out %lld elements), be multiples "
+                    "of 8 (q, kv) or 4 (out) and at most 2^24 (q, kv)",
+                    name, (long long)qw, (long long)kw, (long long)qw);
+    if (seq_q == 0) return ok();
+    if (!q || !q_positions || !out || !lse)
+        return fail(CPATTN_ERR_INVALID_ARG, "%s: q, q_positions, out and lse must be non-NULL", name);
+    if (seq_kv > 0 && (!k || !v || !kv_positions))
+        return fail(CPATTN_ERR_INVALID_ARG, "%s: k, v and kv_positions must be non-NULL", name);
+    if (!aligned16(q) || !aligned16(out) || (seq_kv > 0 && (!aligned16(k) || !aligned16(v))))
+        return fail(CPATTN_ERR_UNSUPPORTED, "%s: q, k, v and out must be 16-byte aligned", name);
+    if ((seq_q + 31) / 32 * (int64_t)heads_kv > kMaxGrid)
+        return fail(CPATTN_ERR_UNSUPPORTED, "%s: launch grid too large", name);
+    // batch 1; no keys is the same kernel with an empty block (it reads no K/V)
+    cpattn::BlockFwdArgs a{q,     k,     v,       q_positions, kv_positions, out,      lse,
+                           1,     seq_q, seq_kv, heads_q,     heads_kv,     head_dim, scale, false};
+    a.n_blk = 1;
+    a.blk[0] = cpattn::KVBlockArg{k, v, kv_positions, seq_kv};
+    a.q_row_stride = q_row_stride;
+    a.kv_row_stride = kv_row_stride;
+    a.out_row_stride = out_row_stride;
+    return from_hip(cpattn::launch_block_fwd_bf16(a, (hipStream_t)stream), name);
+}
+
 CPATTN_API cpattn_status_t cpattn_attn_bwd_delta(const float* out, const void* dout, cpattn_dtype_t dtype,
                                                  int32_t batch, int64_t seq, int32_t heads, int32_t head_dim,
                                                  float* delta, void* stream) {

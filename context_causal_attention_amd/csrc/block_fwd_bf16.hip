@@ -103,6 +103,9 @@ struct Params {
     float c;           // scale * log2(e)
     int32_t merge;     // merge into (out, lse) instead of overwriting them
     int32_t n_blk;     // K/V blocks attended in turn, as one softmax over all their keys
+    int64_t q_rs;      // elements between consecutive rows of q, K/V and out (heads within a
+    int64_t kv_rs;     // row are contiguous: dense rows have heads * kD)
+    int64_t out_rs;
     KVBlock blk[kMaxBlocks];
 };
 
@@ -237,13 +240,13 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
     // (1 KB) per instruction; lane -> row (lane >> 4), stored chunk (lane & 15).  The source
     // address is a wave-uniform tile base plus a per-lane byte offset fixed for the kernel;
     // only a ragged last tile clamps its rows (to the last key, finite data the mask hides).
-    const int64_t kvstride = (int64_t)p.heads_kv * kD;  // elements between consecutive keys
+    const int64_t kvstride = p.kv_rs;  // elements between consecutive keys
     const int64_t tile_bytes_g = (int64_t)kBN * kvstride * 2;  // global bytes between tiles
     auto kbase_of = [&](int o) {
-        return (const char*)(p.blk[o].k + (b * p.blk[o].seq * p.heads_kv + kvh) * (int64_t)kD);
+        return (const char*)(p.blk[o].k + b * p.blk[o].seq * p.kv_rs + kvh * (int64_t)kD);
     };
     auto vbase_of = [&](int o) {
-        return (const char*)(p.blk[o].v + (b * p.blk[o].seq * p.heads_kv + kvh) * (int64_t)kD);
+        return (const char*)(p.blk[o].v + b * p.blk[o].seq * p.kv_rs + kvh * (int64_t)kD);
     };
     constexpr int kLW = NWR < 8 ? NWR : 8;  // waves of a row group that load (all, or the first 8)
     constexpr int kRowsPerWave = kBN / kLW;
@@ -302,7 +305,7 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
         myh[nb] = head;
         const bool valid = i < p.seq_q;
         mypos[nb] = valid ? p.qpos[i] : INT64_MIN;
-        const __bf16* qrow = p.q + ((b * p.seq_q + (valid ? i : 0)) * p.heads_q + head) * kD + 8 * half;
+        const __bf16* qrow = p.q + (b * p.seq_q + (valid ? i : 0)) * p.q_rs + head * kD + 8 * half;
 #pragma unroll
         for (int ks = 0; ks < kD / 16; ++ks) {
             u32x4 raw = valid ? *(const u32x4*)(qrow + 16 * ks) : u32x4{0, 0, 0, 0};
@@ -585,7 +588,7 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
         const bool any = l_tot > 0.f;
         const float inv = any ? 1.f / l_tot : 0.f;
         if (myq[nb] >= p.seq_q) continue;
-        float* orow = p.out + ((b * p.seq_q + myq[nb]) * p.heads_q + myh[nb]) * kD;
+        float* orow = p.out + (b * p.seq_q + myq[nb]) * p.out_rs + myh[nb] * kD;
         float* lrow = p.lse + (b * p.heads_q + myh[nb]) * p.seq_q + myq[nb];
         const float lse_t = any ? (m_run[nb] + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
         if (p.merge) {
@@ -641,6 +644,9 @@ hipError_t launch_block_fwd_bf16(const BlockFwdArgs& a, hipStream_t stream) {
     p.lse = a.lse;
     p.seq_q = a.seq_q;
     p.n_blk = a.n_blk;
+    p.q_rs = a.q_row_stride > 0 ? a.q_row_stride : (int64_t)a.heads_q * kD;
+    p.kv_rs = a.kv_row_stride > 0 ? a.kv_row_stride : (int64_t)a.heads_kv * kD;
+    p.out_rs = a.out_row_stride > 0 ? a.out_row_stride : (int64_t)a.heads_q * kD;
     for (int o = 0; o < a.n_blk; ++o)
         p.blk[o] = KVBlock{(const __bf16*)a.blk[o].k, (const __bf16*)a.blk[o].v, a.blk[o].pos, a.blk[o].seq};
     p.heads_q = a.heads_q;

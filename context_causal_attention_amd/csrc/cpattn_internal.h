@@ -55,6 +55,11 @@ struct BlockFwdArgs {
     // block call fills blk[0] from k, v, kv_pos, seq_kv
     int32_t n_blk;
     KVBlockArg blk[kMaxRingBlocks];
+    // bf16 path: elements between consecutive sequence rows of q, of every K/V block, and of
+    // out (heads are contiguous within a row); 0 means dense rows (heads * head_dim)
+    int64_t q_row_stride = 0;
+    int64_t kv_row_stride = 0;
+    int64_t out_row_stride = 0;
 };
 
 // No keys: writes out = 0 and lse = -inf for every row (merge: merges that empty result).

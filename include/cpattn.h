@@ -151,6 +151,37 @@ cpattn_status_t cpattn_block_fwd_merge(const void* q, const void* k, const void*
                                        float* lse, void* stream);
 
 /*
+ * cpattn_block_fwd_rows -- cpattn_block_fwd (bf16, batch 1, head_dim 128) on strided rows:
+ * q, k, v and out are sequences of rows whose consecutive rows lie q_row_stride,
+ * kv_row_stride and out_row_stride elements apart; within a row the heads are contiguous
+ * (head h at h * 128).  This lets Ulysses' head group be read in place from the stacked
+ * rank shards and its output written back into them: with B = 1 and contiguous shards,
+ * the exchange of [HB] "Ulysses" / [OLMO] Eq. (96) maps global row i of group g to row i
+ * of the stacked buffer at head offset g * H/C, so q = Q_st + g*(Hq/C)*128 with
+ * q_row_stride = Hq*128 (likewise k, v and out), and the sequence->heads permute and its
+ * inverse need no separate pass.  Results have the same bits as cpattn_block_fwd on dense
+ * copies of the same rows.
+ *   q        in  bf16 rows of heads_q*128 values, seq_q rows
+ *   k, v     in  bf16 rows of heads_kv*128 values, seq_kv rows
+ *   q_row_stride, kv_row_stride   in elements: >= heads*128, multiples of 8, <= 2^24
+ *   q_positions, kv_positions, scale   as for cpattn_block_fwd
+ *   out      out fp32 rows, out_row_stride elements apart (>= heads_q*128, multiple of 4);
+ *                only each row's heads_q*128 values are written
+ *   lse      out fp32 [heads_q][seq_q] (dense)
+ * seq_q == 0 is a no-op; seq_kv == 0 gives out = 0 and lse = -inf (k, v, kv_positions may
+ * then be NULL).  Pointers 16-byte aligned.
+ * Errors: INVALID_ARG (NULL pointer, heads <= 0, seq < 0, bad scale), SHAPE (heads_q %
+ * heads_kv != 0), UNSUPPORTED (head_dim != 128, a stride too small, too large or not a
+ * multiple of its unit, misalignment).
+ */
+cpattn_status_t cpattn_block_fwd_rows(const void* q, int64_t q_row_stride, const void* k,
+                                      const void* v, int64_t kv_row_stride, int64_t seq_q,
+                                      int64_t seq_kv, int32_t heads_q, int32_t heads_kv,
+                                      int32_t head_dim, const int64_t* q_positions,
+                                      const int64_t* kv_positions, float scale, float* out,
+                                      int64_t out_row_stride, float* lse, void* stream);
+
+/*
  * cpattn_ring_share_fwd -- a rank's whole share in one launch: the queries against C K/V
  * blocks taken in the given (ring) order, as [CP] "Peer-to-peer" / "Forward" computes them
  * step by step with the merge of attention tiles.  Here each workgroup walks the blocks'

@@ -244,3 +244,34 @@ def test_ring_share_fwd_validation(lib):
     # the fp32 path checks each block as a single-block call does
     assert _rs(lib, dtype=0, d=96) == UNSUPPORTED
     assert _rs(lib, dtype=0, hq=6, hkv=4) == SHAPE
+
+
+def _rows(lib, **kw):
+    a = dict(q=FAKE, qs=512, k=FAKE, v=FAKE, ks=128, sq=64, skv=64, hq=4, hkv=1, d=128, qpos=FAKE, kvpos=FAKE,
+             scale=0.1, out=FAKE, os=512, lse=FAKE)
+    a.update(kw)
+    return lib.cpattn_block_fwd_rows(a["q"], a["qs"], a["k"], a["v"], a["ks"], a["sq"], a["skv"], a["hq"], a["hkv"],
+                                     a["d"], a["qpos"], a["kvpos"], a["scale"], a["out"], a["os"], a["lse"], NULL)
+
+
+def test_block_fwd_rows_validation(lib):
+    assert _rows(lib, hq=0) == INVALID
+    assert _rows(lib, sq=-1) == INVALID
+    assert _rows(lib, scale=float("nan")) == INVALID
+    assert _rows(lib, hq=6, hkv=4, qs=768, ks=512, os=768) == SHAPE
+    assert _rows(lib, d=64) == UNSUPPORTED
+    # row strides: at least a row, multiples of 8 (q, k/v) or 4 (out), q and k/v at most 2^24
+    assert _rows(lib, qs=504) == UNSUPPORTED and "row strides" in _err(lib)
+    assert _rows(lib, ks=120) == UNSUPPORTED
+    assert _rows(lib, qs=1028) == UNSUPPORTED
+    assert _rows(lib, ks=(1 << 24) + 8) == UNSUPPORTED
+    assert _rows(lib, os=510) == UNSUPPORTED
+    assert _rows(lib, q=NULL) == INVALID
+    assert _rows(lib, lse=NULL) == INVALID
+    assert _rows(lib, kvpos=NULL) == INVALID
+    assert _rows(lib, out=ctypes.c_void_p(0x1004)) == UNSUPPORTED
+    assert _rows(lib, k=ctypes.c_void_p(0x1008)) == UNSUPPORTED
+    assert _rows(lib, sq=0, q=NULL, out=NULL, lse=NULL, qpos=NULL) == OK
+    # (larger strides than the row pass validation: the call would then launch, so a grid
+    # bound stands in for it here)
+    assert _rows(lib, qs=4096, ks=1024, os=4100, sq=1 << 40) == UNSUPPORTED and "grid" in _err(lib)

@@ -238,3 +238,36 @@ def test_random_shapes_sampled(seed):
     empty = np.isneginf(ref_l)
     assert np.array_equal(np.isneginf(lv), empty)
     assert np.all(out[:, rows].cpu().numpy().transpose(0, 2, 1, 3)[empty] == 0.0)
+
+
+@pytest.mark.parametrize("S,Hq,Hkv,shared", [(6000, 32, 8, True), (6000, 32, 8, False), (300, 8, 2, True),
+                                             (777, 4, 4, False)])
+def test_block_fwd_rows_equals_dense(S, Hq, Hkv, shared):
+    """cpattn_block_fwd_rows on one head group of wider rows (q, k, v read in place; out written
+    into a wider buffer) gives the bits of cpattn_block_fwd on dense copies, and leaves the
+    other heads of out untouched."""
+    D, scale = 128, 1 / math.sqrt(128)
+    q_all, k_all, v_all = _inputs(S + Hq, 1, S, S, 2 * Hq, 2 * Hkv, D, torch.bfloat16)
+    q_all, k_all, v_all = (x[0].to(DEV) for x in (q_all, k_all, v_all))
+    qv, kv, vv = q_all[:, Hq:], k_all[:, Hkv:], v_all[:, Hkv:]
+    out_all = torch.full((S, 2 * Hq, D), 7.0, device=DEV)
+    ov = out_all[:, Hq:]
+    tp = torch.arange(S, device=DEV)
+    tk = tp if shared else tp.clone()
+    _, lse = cp.block_fwd_rows(qv, kv, vv, tp, tk, scale, ov)
+    ref_o, ref_l = cp.block_fwd(qv.contiguous()[None], kv.contiguous()[None], vv.contiguous()[None], tp, tk, scale)
+    torch.cuda.synchronize()
+    assert torch.equal(ov, ref_o[0]) and torch.equal(lse, ref_l)
+    assert bool((out_all[:, :Hq] == 7.0).all())
+
+
+def test_block_fwd_rows_no_keys():
+    q = _inputs(3, 1, 50, 1, 8, 2, 128, torch.bfloat16)[0][0].to(DEV)
+    out = torch.full((50, 16, 128), 5.0, device=DEV)
+    _, lse = cp.block_fwd_rows(q[:, :], torch.empty((0, 2, 128), dtype=torch.bfloat16, device=DEV),
+                               torch.empty((0, 2, 128), dtype=torch.bfloat16, device=DEV),
+                               torch.arange(50, device=DEV), torch.zeros(0, dtype=torch.int64, device=DEV), 0.1,
+                               out[:, 8:])
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out[:, 8:]) == 0 and bool((out[:, :8] == 5.0).all())
+    assert bool(torch.isneginf(lse).all())
