@@ -15,8 +15,9 @@
  * - All tensor pointers are DEVICE pointers owned by the caller.  The library never
  *   allocates, frees or synchronises; every call only enqueues kernels on `stream`
  *   (a hipStream_t passed as void*; NULL means the null stream) and returns.
- * - Tensors are dense, row-major, in the layouts stated per call.  Outputs must not alias
- *   inputs, except where a call is documented as in place.
+ * - Tensors are dense, row-major, in the layouts stated per call (cpattn_block_fwd_rows
+ *   alone takes row strides).  Outputs must not alias inputs, except where a call is
+ *   documented as in place.
  * - Every argument is validated on the host before anything is enqueued.  A call that
  *   returns an error has enqueued nothing and touched no memory.  CPATTN_ERR_HIP is
  *   returned when the HIP runtime reports an error for a launch.
