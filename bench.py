@@ -59,9 +59,9 @@ def parse_args(argv=None):
     ap.add_argument("--mode", choices=("single", "fused", "unfused"), default="single",
                     help="ring share: one launch over all ring blocks (single), one launch per step "
                          "merging in its epilogue (fused), or per-step tiles plus the merge kernel "
-                         "(unfused); Ulysses with one batch and contiguous shards: unfused runs the "
-                         "exchanges as separate permute kernels instead of the attention's row "
-                         "addressing")
+                         "(unfused); Ulysses: the workload's explicit permute kernels around the "
+                         "attention (default), or, with one batch and contiguous shards, the "
+                         "exchanges as the attention's row addressing (fused)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--no-sclk", action="store_true",
@@ -150,7 +150,7 @@ class Plan:
             S = w.seq_len
             # one batch, contiguous shards: global row i of the group is row i of the stacked
             # buffers at the group's head offset, so the attention reads and writes them in place
-            self.rows = mode != "unfused" and w.batch == 1 and not w.zigzag and td == torch.bfloat16
+            self.rows = mode == "fused" and w.batch == 1 and not w.zigzag and td == torch.bfloat16
             if self.rows:
                 Hq, Hk = w.heads_q, w.heads_kv
                 self.qrows = self.qst.view(S, Hq, w.head_dim)[:, g * hq:(g + 1) * hq]
