@@ -275,3 +275,15 @@ def test_block_fwd_rows_validation(lib):
     # (larger strides than the row pass validation: the call would then launch, so a grid
     # bound stands in for it here)
     assert _rows(lib, qs=4096, ks=1024, os=4100, sq=1 << 40) == UNSUPPORTED and "grid" in _err(lib)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without libcpattn.so every entry point raises: there is no fallback path."""
+    import context_causal_attention_amd._binding as b
+    monkeypatch.setattr(b, "_lib", None)
+    monkeypatch.setattr(b, "LIB_PATH", tmp_path / "libcpattn.so")
+    with pytest.raises(RuntimeError, match="not built"):
+        b.load_library()
+    import torch
+    with pytest.raises(RuntimeError, match="not built"):
+        b.zigzag_index(64, 4, 0, out=torch.empty(16, dtype=torch.int64))
