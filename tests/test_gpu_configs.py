@@ -142,7 +142,7 @@ def test_ulysses_gqa_128k_group():
     print(f"ulysses_gqa_128k: max abs err O {eo:.3g}, lse {el:.3g} over {len(rows)} rows")
     tol_o, tol_l = TOL[w.dtype]
     assert eo <= tol_o and el <= tol_l
-    # the exchanges folded into the attention's row addressing (the bench's default form):
+    # the exchanges folded into the attention's row addressing (the bench's --mode fused form):
     # the same bits in the same stacked output, the other groups' heads untouched
     out_rows = torch.zeros_like(out_stacked)
     og_r, lse_r = cp.ulysses_share_fwd(stack(qfull).to(DEV), stack(kfull).to(DEV), stack(vfull).to(DEV), g,

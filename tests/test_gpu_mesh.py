@@ -67,6 +67,33 @@ def test_ulysses_zigzag_share_small_every_row():
     assert np.array_equal(out_st.cpu().numpy(), ref_st)
 
 
+@pytest.mark.parametrize("B,fused", [(1, None), (1, False), (2, None)])
+def test_ulysses_contiguous_share_small_every_row(B, fused):
+    # contiguous shards: with B = 1 the exchanges fold into the attention's row addressing,
+    # with B = 2 (or fused=False) they run as explicit permutes; both against the oracle
+    w = Workload("u_small", "ulysses", B, 1024, 8, 4, 128, "bf16", 4, group=2)
+    C, g, s = w.cp_size, w.group, w.local_len
+    ids = range(2 * C)
+    full = {n: gen(w, n, ids, h) for n, h in (("q", w.heads_q), ("k", w.heads_kv), ("v", w.heads_kv))}
+    stack = lambda x: x.reshape(B, C, s, *x.shape[2:]).transpose(0, 1).contiguous().to(DEV)
+    out_st = torch.zeros((C, B, s, w.heads_q, 128), device=DEV)
+    og, lse = cp.ulysses_share_fwd(stack(full["q"]), stack(full["k"]), stack(full["v"]), g, w.scale, out_st,
+                                   zigzag=False, fused=fused)
+    torch.cuda.synchronize()
+    hq, hk = w.heads_q // C, w.heads_kv // C
+    pos = np.arange(w.seq_len, dtype=np.int64)
+    ref_o, ref_l = oracle.attention_rows(full["q"][:, :, g * hq:(g + 1) * hq].float().numpy(),
+                                         full["k"][:, :, g * hk:(g + 1) * hk].float().numpy(),
+                                         full["v"][:, :, g * hk:(g + 1) * hk].float().numpy(), pos, pos, w.scale)
+    tol_o, tol_l = TOL["bf16"]
+    assert max_abs(og.cpu().numpy(), ref_o) <= tol_o
+    assert max_abs(lse.cpu().numpy(), ref_l) <= tol_l
+    # the group's heads of every shard hold the group output, the other heads stay zero
+    back = out_st.transpose(0, 1).reshape(B, w.seq_len, w.heads_q, 128).cpu()
+    assert torch.equal(back[:, :, g * hq:(g + 1) * hq], og.cpu())
+    assert torch.count_nonzero(back[:, :, :g * hq]) == 0 and torch.count_nonzero(back[:, :, (g + 1) * hq:]) == 0
+
+
 def _usp_inputs(w):
     A, C = w.a2a, w.cp_size
     R = C // A
