@@ -104,7 +104,9 @@ cpattn_status_t block_fwd_common(const char* name, bool merge, const void* q, co
         return fail(CPATTN_ERR_UNSUPPORTED, "%s: bf16 path needs 16-byte aligned q, k, v, out", name);
     if (dtype == CPATTN_F32 && ((seq_q + 63) / 64 > kMaxGrid || heads_q > 65535 || batch > 65535))
         return fail(CPATTN_ERR_UNSUPPORTED, "%s: launch grid too large", name);
-    if (dtype == CPATTN_BF16 && (seq_q + 31) / 32 * (int64_t)batch * heads_kv > kMaxGrid)
+    // every bf16 forward variant launches ceil(seq_q / pq) * batch * heads_q / G blocks with
+    // pq >= 32 query positions per block, so this bound holds for all of them
+    if (dtype == CPATTN_BF16 && (seq_q + 31) / 32 * (int64_t)batch * heads_q > kMaxGrid)
         return fail(CPATTN_ERR_UNSUPPORTED, "%s: launch grid too large", name);
     cpattn::BlockFwdArgs a{q,     k,      v,       q_positions, kv_positions, out,      lse,
                            batch, seq_q, seq_kv, heads_q,     heads_kv,     head_dim, scale, merge};
@@ -169,7 +171,7 @@ CPATTN_API cpattn_status_t cpattn_block_fwd_rows(const void* q, int64_t q_row_st
         return fail(CPATTN_ERR_INVALID_ARG, "%s: k, v and kv_positions must be non-NULL", name);
     if (!aligned16(q) || !aligned16(out) || (seq_kv > 0 && (!aligned16(k) || !aligned16(v))))
         return fail(CPATTN_ERR_UNSUPPORTED, "%s: q, k, v and out must be 16-byte aligned", name);
-    if ((seq_q + 31) / 32 * (int64_t)heads_kv > kMaxGrid)
+    if ((seq_q + 31) / 32 * (int64_t)heads_q > kMaxGrid)  // as for block_fwd
         return fail(CPATTN_ERR_UNSUPPORTED, "%s: launch grid too large", name);
     // batch 1; no keys is the same kernel with an empty block (it reads no K/V)
     cpattn::BlockFwdArgs a{q,     k,     v,       q_positions, kv_positions, out,      lse,
@@ -308,7 +310,7 @@ CPATTN_API cpattn_status_t cpattn_ring_share_fwd(const void* q, const void* cons
         return fail(CPATTN_ERR_INVALID_ARG, "%s: q, q_positions, out and lse must be non-NULL", name);
     if (!aligned16(q) || !aligned16(out))
         return fail(CPATTN_ERR_UNSUPPORTED, "%s: bf16 path needs 16-byte aligned q and out", name);
-    if ((seq_q + 31) / 32 * (int64_t)batch * heads_kv > kMaxGrid)
+    if ((seq_q + 31) / 32 * (int64_t)batch * heads_q > kMaxGrid)  // as for block_fwd
         return fail(CPATTN_ERR_UNSUPPORTED, "%s: launch grid too large", name);
     cpattn::BlockFwdArgs a{q, nullptr, nullptr, q_positions, nullptr, out,      lse,   batch,
                            seq_q, 0,   heads_q, heads_kv,    head_dim, scale,   false};

@@ -76,6 +76,9 @@ def test_block_fwd_validation(lib):
     assert _bf(lib, out=NULL) == INVALID
     assert _bf(lib, kvpos=NULL) == INVALID
     assert _bf(lib, q=ctypes.c_void_p(0x1002)) == UNSUPPORTED  # misaligned for 16-byte loads
+    # the grid counts query heads: 2^27 query tiles of 32 rows times 16 query heads is past the
+    # grid limit even though the one K/V head alone would fit
+    assert _bf(lib, seq_q=1 << 32, seq_kv=64, hq=16, hkv=1) == UNSUPPORTED and "grid" in _err(lib)
     # an empty query set is a valid no-op that never touches the GPU
     assert _bf(lib, seq_q=0, q=NULL, out=NULL, lse=NULL, qpos=NULL) == OK
 
