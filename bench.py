@@ -97,7 +97,9 @@ class Plan:
             self.qs = {r: synthetic.chunks("q", [r, 2 * C - 1 - r], heads=w.heads_q, **kw).to(dev) for r in self.ranks}
             self.k = [synthetic.chunks("k", [o, 2 * C - 1 - o], heads=w.heads_kv, **kw).to(dev) for o in range(C)]
             self.v = [synthetic.chunks("v", [o, 2 * C - 1 - o], heads=w.heads_kv, **kw).to(dev) for o in range(C)]
-            self.pos = [torch.empty(w.local_len, dtype=torch.int64, device=dev) for _ in range(C)]
+            # every owner's positions, one row each, written by one launch per step
+            self.pos_all = torch.empty((C, w.local_len), dtype=torch.int64, device=dev)
+            self.pos = list(self.pos_all.unbind(0))
             self.out = torch.empty((w.batch, w.local_len, w.heads_q, w.head_dim), dtype=torch.float32, device=dev)
             self.lse = torch.empty((w.batch, w.heads_q, w.local_len), dtype=torch.float32, device=dev)
             if mode == "unfused":
@@ -116,7 +118,9 @@ class Plan:
             self.kseq = torch.empty_like(self.kg)
             self.vseq = torch.empty_like(self.vg)
             self.qs = [synthetic.chunks("q", [rr, 2 * C - 1 - rr], heads=w.heads_q, **kw).to(dev) for rr in range(C)]
-            self.pos = [torch.empty(w.local_len, dtype=torch.int64, device=dev) for _ in range(C)]
+            # every owner's positions, one row each, written by one launch per step
+            self.pos_all = torch.empty((C, w.local_len), dtype=torch.int64, device=dev)
+            self.pos = list(self.pos_all.unbind(0))
             self.gpos = torch.arange(w.seq_len, device=dev)
             self.out = torch.empty((w.batch, w.local_len, w.heads_q, w.head_dim), dtype=torch.float32, device=dev)
             self.lse = torch.empty((w.batch, w.heads_q, w.local_len), dtype=torch.float32, device=dev)
@@ -235,8 +239,7 @@ class Plan:
                 fn(*a, **kw)
 
         if self.kind == "ring_share":
-            for o in range(C):
-                cp.zigzag_index(w.seq_len, C, o, out=self.pos[o])
+            cp.zigzag_index_all(w.seq_len, C, out=self.pos_all)
             for r in self.ranks:
                 q = self.qs[r]
                 order = [(r - step) % C for step in range(C)]
@@ -258,8 +261,8 @@ class Plan:
             nb = 2 * self.kg.numel() * self.kg.element_size()
             hbm("reorder_kernel", nb, cp.reorder_gathered, self.kg, C, cp.RANK_TO_SEQ, out=self.kseq)
             hbm("reorder_kernel", nb, cp.reorder_gathered, self.vg, C, cp.RANK_TO_SEQ, out=self.vseq)
+            cp.zigzag_index_all(w.seq_len, C, out=self.pos_all)
             for rr in range(C):
-                cp.zigzag_index(w.seq_len, C, rr, out=self.pos[rr])
                 attn(self.qs[rr], self.kseq, self.vseq, self.pos[rr], self.gpos, w.scale, self.out, self.lse)
         elif self.kind == "ulysses" and self.rows:
             attn(self.qrows, self.krows, self.vrows, self.gpos, self.gpos, w.scale, self.orows, self.lg,

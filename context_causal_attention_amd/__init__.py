@@ -31,4 +31,5 @@ from ._binding import (  # noqa: F401
     ulysses_share_fwd,
     usp_share_fwd,
     zigzag_index,
+    zigzag_index_all,
 )

@@ -53,6 +53,7 @@ def load_library():
     L.cpattn_abi_version.argtypes = []
     L.cpattn_abi_version.restype = i32
     L.cpattn_zigzag_index.argtypes = [i64, i32, i32, P, P]
+    L.cpattn_zigzag_index_all.argtypes = [i64, i32, P, P]
     L.cpattn_block_fwd.argtypes = [P, P, P, ctypes.c_int, i32, i64, i64, i32, i32, i32, P, P, f32, P, P, P]
     L.cpattn_block_fwd_merge.argtypes = list(L.cpattn_block_fwd.argtypes)
     L.cpattn_block_fwd_rows.argtypes = [P, i64, P, P, i64, i64, i64, i32, i32, i32, P, P, f32, P, i64, P, P]
@@ -64,7 +65,7 @@ def load_library():
     L.cpattn_reorder_gathered.argtypes = [P, P, i32, i64, i64, i32, ctypes.c_int, P]
     L.cpattn_ulysses_permute.argtypes = [P, P, i32, i32, i64, i32, i32, i32, i32, ctypes.c_int, P]
     L.cpattn_ulysses_permute_zigzag.argtypes = list(L.cpattn_ulysses_permute.argtypes)
-    for name in ("cpattn_zigzag_index", "cpattn_block_fwd", "cpattn_block_fwd_merge", "cpattn_block_fwd_rows",
+    for name in ("cpattn_zigzag_index", "cpattn_zigzag_index_all", "cpattn_block_fwd", "cpattn_block_fwd_merge", "cpattn_block_fwd_rows",
                  "cpattn_lse_merge",
                  "cpattn_attn_bwd_delta", "cpattn_block_bwd", "cpattn_ring_share_fwd",
                  "cpattn_reorder_gathered", "cpattn_ulysses_permute", "cpattn_ulysses_permute_zigzag"):
@@ -115,6 +116,20 @@ def zigzag_index(seq_len: int, cp_size: int, rank: int, out: torch.Tensor | None
                           device=device if device is not None else torch.device("cuda"))
     _need(out, "out", torch.int64)
     _check(L.cpattn_zigzag_index(seq_len, cp_size, rank, _ptr(out), _stream(out.device)))
+    return out
+
+
+def zigzag_index_all(seq_len: int, cp_size: int, out: torch.Tensor | None = None,
+                     device=None) -> torch.Tensor:
+    """Every rank's zigzag positions in one launch: int64 [cp_size, seq_len / cp_size], row r
+    being rank r's local tokens."""
+    L = load_library()
+    n = seq_len // max(cp_size, 1)
+    if out is None:
+        out = torch.empty((max(cp_size, 1), n), dtype=torch.int64,
+                          device=device if device is not None else torch.device("cuda"))
+    _need(out, "out", torch.int64, shape=(cp_size, n))
+    _check(L.cpattn_zigzag_index_all(seq_len, cp_size, _ptr(out), _stream(out.device)))
     return out
 
 

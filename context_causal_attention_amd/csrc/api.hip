@@ -70,6 +70,20 @@ CPATTN_API cpattn_status_t cpattn_zigzag_index(int64_t seq_len, int32_t cp_size,
                     "zigzag_index");
 }
 
+CPATTN_API cpattn_status_t cpattn_zigzag_index_all(int64_t seq_len, int32_t cp_size, int64_t* positions,
+                                                   void* stream) {
+    if (seq_len <= 0) return fail(CPATTN_ERR_INVALID_ARG, "zigzag_index_all: seq_len must be > 0");
+    if (cp_size <= 0) return fail(CPATTN_ERR_INVALID_ARG, "zigzag_index_all: cp_size must be > 0");
+    if (cp_size > 65535) return fail(CPATTN_ERR_UNSUPPORTED, "zigzag_index_all: cp_size above 65535");
+    if (!positions) return fail(CPATTN_ERR_INVALID_ARG, "zigzag_index_all: positions is NULL");
+    if (seq_len % (2 * (int64_t)cp_size) != 0)
+        return fail(CPATTN_ERR_SHAPE, "zigzag_index_all: seq_len %lld not divisible by 2*cp_size = %lld",
+                    (long long)seq_len, 2LL * cp_size);
+    const int64_t t = seq_len / (2 * (int64_t)cp_size);
+    return from_hip(cpattn::launch_zigzag_index_all(t, cp_size, positions, (hipStream_t)stream),
+                    "zigzag_index_all");
+}
+
 namespace {
 
 // cpattn_block_fwd (merge = false) and cpattn_block_fwd_merge (merge = true) share their

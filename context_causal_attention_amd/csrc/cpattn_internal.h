@@ -8,6 +8,8 @@
 
 namespace cpattn {
 
+hipError_t launch_zigzag_index_all(int64_t chunk_len, int32_t cp_size, int64_t* positions,
+                                   hipStream_t stream);
 hipError_t launch_zigzag_index(int64_t chunk_len, int64_t early_chunk, int64_t late_chunk,
                                int64_t* positions, hipStream_t stream);
 

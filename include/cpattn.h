@@ -86,6 +86,18 @@ cpattn_status_t cpattn_zigzag_index(int64_t seq_len, int32_t cp_size, int32_t ra
                                     int64_t* positions, void* stream);
 
 /*
+ * cpattn_zigzag_index_all -- the same positions for every rank in one launch (the ring
+ * forward of [CP] "Peer-to-peer" needs each ring step's owner's positions, i.e. all ranks').
+ *
+ *   positions  out, int64 [cp_size][seq_len / cp_size], caller-owned: row r equals what
+ *              cpattn_zigzag_index(seq_len, cp_size, r, ...) writes.  Rows are contiguous.
+ * Errors: as cpattn_zigzag_index (no rank argument); UNSUPPORTED if cp_size > 65535 (one
+ * grid row per rank).
+ */
+cpattn_status_t cpattn_zigzag_index_all(int64_t seq_len, int32_t cp_size, int64_t* positions,
+                                        void* stream);
+
+/*
  * cpattn_block_fwd -- attention of local queries against one K/V block under a causal
  * mask on GLOBAL positions, returning the block's normalised output and its log-sum-exp.
  * This is the per-step attention call of the ring forward in [CP] "Peer-to-peer" /

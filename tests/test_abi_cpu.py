@@ -49,6 +49,12 @@ def test_zigzag_validation(lib):
     assert f(32, 0, 0, FAKE, NULL) == INVALID
     assert f(0, 4, 0, FAKE, NULL) == INVALID
     assert f(32, 4, 0, NULL, NULL) == INVALID
+    g = lib.cpattn_zigzag_index_all
+    assert g(30, 4, FAKE, NULL) == SHAPE and "divisible" in _err(lib)
+    assert g(32, 0, FAKE, NULL) == INVALID
+    assert g(0, 4, FAKE, NULL) == INVALID
+    assert g(32, 4, NULL, NULL) == INVALID
+    assert g(1 << 20, 65536, FAKE, NULL) == UNSUPPORTED  # one grid row per rank
 
 
 def _bf(lib, **kw):

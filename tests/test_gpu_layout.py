@@ -23,6 +23,18 @@ def test_zigzag_index_bit_exact(S, C):
         assert np.array_equal(got, oracle.zigzag_positions(S, C, r)), (S, C, r)
 
 
+@pytest.mark.parametrize("S,C", [(256, 4), (8192, 4), (262144, 8), (48, 3), (2, 1), (64, 16), (1 << 20, 32)])
+def test_zigzag_index_all_bit_exact(S, C):
+    # every row of the one-launch form against the oracle; a guard row after the buffer's end
+    # stays untouched
+    buf = torch.full((C + 1, S // C), -7, dtype=torch.int64, device=DEV)
+    cp.zigzag_index_all(S, C, out=buf[:C])
+    got = buf.cpu().numpy()
+    for r in range(C):
+        assert np.array_equal(got[r], oracle.zigzag_positions(S, C, r)), (S, C, r)
+    assert (got[C] == -7).all()
+
+
 @pytest.mark.parametrize("C,t,B,row", [(4, 3, 2, 7), (4, 5, 1, 256), (8, 2, 3, 16), (3, 7, 2, 48),
                                        (1, 4, 1, 32), (16, 1, 1, 5)])
 def test_reorder_bit_exact_small(C, t, B, row):
