@@ -177,7 +177,8 @@ class Plan:
             self.qh = torch.empty((w.batch, n, hq, w.head_dim), dtype=td, device=dev)
             self.kh = [torch.empty((w.batch, n, hk, w.head_dim), dtype=td, device=dev) for _ in range(R)]
             self.vh = [torch.empty((w.batch, n, hk, w.head_dim), dtype=td, device=dev) for _ in range(R)]
-            self.pos = [torch.empty(n, dtype=torch.int64, device=dev) for _ in range(R)]
+            self.pos_all = torch.empty((R, n), dtype=torch.int64, device=dev)
+            self.pos = list(self.pos_all.unbind(0))
             self.out = torch.empty((w.batch, n, hq, w.head_dim), dtype=torch.float32, device=dev)
             self.lse = torch.empty((w.batch, hq, n), dtype=torch.float32, device=dev)
             self.ost = torch.zeros((A, w.batch, w.local_len, w.heads_q, w.head_dim), dtype=torch.float32,
@@ -286,7 +287,7 @@ class Plan:
                     zigzag=True)
                 hbm("ulysses_kernel", nb(self.vh[o]), cp.ulysses_seq_to_heads, self.vsts[o], a, out=self.vh[o],
                     zigzag=True)
-                cp.zigzag_index(w.seq_len, R, o, out=self.pos[o])
+            cp.zigzag_index_all(w.seq_len, R, out=self.pos_all)
             for step in range(R):
                 owner = (g - step) % R
                 a_ = (self.qh, self.kh[owner], self.vh[owner], self.pos[g], self.pos[owner], w.scale)

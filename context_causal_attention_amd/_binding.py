@@ -414,7 +414,7 @@ def usp_share_fwd(q_st: torch.Tensor, k_sts, v_sts, ring_rank: int, head_group: 
     qh = ulysses_seq_to_heads(q_st, head_group, zigzag=True)
     kh = [ulysses_seq_to_heads(k, head_group, zigzag=True) for k in k_sts]
     vh = [ulysses_seq_to_heads(v, head_group, zigzag=True) for v in v_sts]
-    pos = [zigzag_index(S, R, o, device=q_st.device) for o in range(R)]
+    pos = list(zigzag_index_all(S, R, device=q_st.device).unbind(0))  # every owner's, one launch
     out, lse = ring_share_fwd(qh, kh, vh, pos, ring_rank, scale)
     ulysses_heads_to_seq(out, head_group, out_st, zigzag=True)
     return out, lse
