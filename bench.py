@@ -69,6 +69,12 @@ def parse_args(argv=None):
     ap.add_argument("--graph", action="store_true",
                     help="capture one step in a HIP graph and time its replays (for launch-bound "
                          "small workloads); the attention launches are then timed as part of the step")
+    ap.add_argument("--extras", default=None,
+                    help="comma-separated workload[:mode] list measured after the main line and reported "
+                         "under 'extra' (default: the Ulysses group and the per-step ring share when the "
+                         "main line is the default one; '' for none)")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="skip the bandwidth-bound kernels' separate timing under the MALL flush")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before the steps, run one plain elementwise copy (torch.neg over fp32, "
                          "cached loads and stores) of this many MiB, as the reference dispatch for "
@@ -298,6 +304,31 @@ class Plan:
             hbm("ulysses_kernel", nb(self.out), cp.ulysses_heads_to_seq, self.out, a, self.ost, zigzag=True)
 
 
+    def hbm_calls(self):
+        """The bandwidth-bound kernels of this plan's step, each as (kernel, algorithmic bytes,
+        callable launching it once on the current stream), for timing them one at a time."""
+        cp, w = self.cp, self.w
+        C = w.cp_size
+        nb = lambda x: 2 * x.numel() * x.element_size()  # noqa: E731  (read + write)
+        calls = []
+        if self.backward:
+            n = self.out.numel() * 4 + self.dout.numel() * self.dout.element_size() + self.delta.numel() * 4
+            calls.append(("delta_kernel", n, lambda: cp.attn_bwd_delta(self.out, self.dout, self.delta)))
+        elif self.kind == "ring_share" and self.mode == "unfused":
+            n = 3 * (self.out.numel() + self.lse.numel()) * 4
+            calls.append(("lse_merge_kernel", n, lambda: cp.lse_merge(self.out, self.lse, self.tout, self.tlse)))
+        elif self.kind == "allgather":
+            calls.append(("reorder_kernel", nb(self.kg),
+                          lambda: cp.reorder_gathered(self.kg, C, cp.RANK_TO_SEQ, out=self.kseq)))
+        elif self.kind == "ulysses" and not self.rows:
+            g, zz = w.group, w.zigzag
+            for name, src, dst in (("q", self.qst, self.qg), ("k", self.kst, self.kgp), ("v", self.vst, self.vgp)):
+                calls.append((f"ulysses_kernel ({name})", nb(dst),
+                              lambda src=src, dst=dst: cp.ulysses_seq_to_heads(src, g, out=dst, zigzag=zz)))
+            calls.append(("ulysses_kernel (out, inverse)", nb(self.og),
+                          lambda: cp.ulysses_heads_to_seq(self.og, g, self.ost, zigzag=zz)))
+        return calls
+
     def step_bwd(self, ev=None):
         """One rank share of the ring backward: delta, then the block backward of each ring
         step (dq written at step 0 and added after; each owner's dk, dv written by its step)."""
@@ -502,6 +533,121 @@ def cpu_baseline(w, budget_s: float, total_pairs: float):
             "extrapolated_full_share_s": total_pairs / (pairs / dt)}
 
 
+def measure(plan, steps: int, warmup: int, graph_mode: bool = False):
+    """Warm up, then time exactly ``steps`` steps with an event at every step boundary (and,
+    without a graph, events around every block attention launch)."""
+    import torch
+    for _ in range(warmup):
+        plan.step()
+    torch.cuda.synchronize()
+    ev = []
+    plan.hbm_ev = []
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    graph = None
+    if graph_mode:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            plan.step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            plan.step()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+    marks[0].record()
+    for i in range(steps):
+        if graph is not None:
+            graph.replay()
+        else:
+            plan.step(ev)
+        marks[i + 1].record()
+    torch.cuda.synchronize()
+    ms_total = marks[0].elapsed_time(marks[-1])
+    ms_steps = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(steps))
+    if graph is not None:  # no events inside the graph: the whole step stands for its launches
+        attn_ms = [m / len(plan.attn_flops) for m in ms_steps for _ in plan.attn_flops]
+    else:
+        attn_ms = [s.elapsed_time(e) for s, e in ev]
+    hbm = {}
+    for name, nbytes, s_, e_ in plan.hbm_ev:
+        d = hbm.setdefault(name, [0, 0.0, 0.0])
+        d[0] += 1
+        d[1] += s_.elapsed_time(e_)
+        d[2] += nbytes
+    hbm_kernels = [{"kernel": k, "calls": c, "bytes_per_call": b / c, "avg_ms": round(ms / c, 4),
+                    "GB/s": round(b / (ms * 1e-3) / 1e9, 1), "frac_of_hbm_peak": round(b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+                   for k, (c, ms, b) in hbm.items()]
+    ms_step = ms_total / steps
+    attn_flops = plan.attn_flops * steps
+    return {"ms_step": ms_step, "ms_steps": ms_steps, "value": plan.flops / (ms_step * 1e-3) / 1e12,
+            "attn_ms": attn_ms, "achieved": sum(attn_flops) / (sum(attn_ms) * 1e-3) / 1e12,
+            "hbm_kernels": hbm_kernels, "graph": graph is not None}
+
+
+def hbm_flushed(plan, reps: int = 5, flush_mib: int = 1024):
+    """Each bandwidth-bound kernel of the plan timed alone, ``reps`` times, with a write of a
+    ``flush_mib`` MiB scratch buffer before every repetition (outside the timed events), so
+    that neither the 256 MB MALL nor the L2 holds its inputs when it starts."""
+    import torch
+    calls = plan.hbm_calls()
+    if not calls:
+        return []
+    scratch = torch.empty((flush_mib << 20) // 4, dtype=torch.float32, device=plan.dev)
+    out = []
+    for name, nbytes, fn in calls:
+        fn()  # warm
+        ms = []
+        for i in range(reps):
+            scratch.fill_(float(i))
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            fn()
+            e.record()
+            torch.cuda.synchronize()
+            ms.append(s.elapsed_time(e))
+        ms.sort()
+        med = ms[len(ms) // 2]
+        out.append({"kernel": name, "bytes_per_call": nbytes, "median_ms": round(med, 4), "min_ms": round(ms[0], 4),
+                    "GB/s": round(nbytes / (med * 1e-3) / 1e9, 1),
+                    "frac_of_hbm_peak": round(nbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                    "flush": f"{flush_mib} MiB scratch write before each of {reps} repetitions"})
+    del scratch
+    return out
+
+
+def workload_name(w, mode: str, bwd: bool, graph: bool) -> str:
+    return (w.name + (f"_{mode}" if mode != "single" and w.kind in ("ring_share", "ulysses") else "")
+            + ("_bwd" if bwd else "") + ("_graph" if graph else ""))
+
+
+def extra_line(name: str, mode: str, steps: int, warmup: int, dev):
+    """One more workload of the same run, reported beside the headline: its step time and
+    TFLOP/s, the attention kernel's own rate and fraction of the bf16 peak, and its
+    bandwidth-bound kernels (in the step, and alone under the MALL flush)."""
+    import torch
+    from context_causal_attention_amd.workloads import WORKLOADS
+    w = WORKLOADS[name]
+    plan = Plan(w, dev, mode=mode)
+    m = measure(plan, steps, warmup)
+    res = {"workload": workload_name(w, mode, False, False), "steps": steps, "ms_per_step": round(m["ms_step"], 4),
+           "ms_per_step_median": round(m["ms_steps"][len(m["ms_steps"]) // 2], 4),
+           "value": round(m["value"], 3), "unit": "TFLOP/s", "pct_of_bf16_peak": round(100.0 * m["value"] / PEAK_BF16_TFLOPS, 2),
+           "attention": {"kernel": "block_fwd_bf16", "achieved": round(m["achieved"], 3), "peak": PEAK_BF16_TFLOPS,
+                         "frac": round(m["achieved"] / PEAK_BF16_TFLOPS, 4),
+                         "avg_launch_ms": round(sum(m["attn_ms"]) / len(m["attn_ms"]), 4), "launches": len(m["attn_ms"])},
+           "hbm_kernels": m["hbm_kernels"], "hbm_kernels_flushed": hbm_flushed(plan),
+           "config": {"seq_len": w.seq_len, "cp_size": w.cp_size, "rank": w.rank, "group": w.group,
+                      "sharding": w.sharding, "heads_q": w.heads_q, "heads_kv": w.heads_kv, "head_dim": w.head_dim,
+                      "unmasked_flops_per_step": plan.flops}}
+    del plan
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
 def main(argv=None) -> int:
     args = parse_args(argv)
     if args.gpus != 1:
@@ -527,47 +673,11 @@ def main(argv=None) -> int:
         torch.neg(src, out=dst)  # reads n bytes, writes n bytes
         del src, dst
     torch.cuda.synchronize()
-    for _ in range(args.warmup):
-        plan.step()
-    torch.cuda.synchronize()
-    ev = []
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    graph = None
-    if args.graph:
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            plan.step()
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            plan.step()
-        torch.cuda.synchronize()
-        graph.replay()
-        torch.cuda.synchronize()
-    marks[0].record()
-    for i in range(args.steps):
-        if graph is not None:
-            graph.replay()
-        else:
-            plan.step(ev)
-        marks[i + 1].record()
-    torch.cuda.synchronize()
+    m = measure(plan, args.steps, args.warmup, graph_mode=args.graph)
     sclk = {"mhz_mean": None, "note": "skipped (--no-sclk)"} if args.no_sclk else sclk_under_load(plan, dev.index or 0)
-    ms_total = marks[0].elapsed_time(marks[-1])
-    ms_step = ms_total / args.steps
-    ms_steps = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
-    value = plan.flops / (ms_step * 1e-3) / 1e12
-    if graph is not None:  # no events inside the graph: the whole step stands for its launches
-        attn_ms = [m / len(plan.attn_flops) for m in ms_steps for _ in plan.attn_flops]
-    else:
-        attn_ms = [s.elapsed_time(e) for s, e in ev]
-    attn_flops = plan.attn_flops * args.steps
-    achieved = sum(attn_flops) / (sum(attn_ms) * 1e-3) / 1e12
-    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
     bwd = args.which == "bwd"
-    kernel = ("block_bwd_dq_kernel+block_bwd_dkdv_kernel" if bwd else "block_fwd_bf16_kernel") \
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    kernel = ("block_bwd_dq_kernel+block_bwd_dkdv_kernel" if bwd else "block_fwd_bf16") \
         if w.dtype == "bf16" else ("bwd_dq_f32_kernel+bwd_dkdv_f32_kernel" if bwd else "block_fwd_f32_kernel")
     props = torch.cuda.get_device_properties(dev)
     max_mhz = _hip_max_sclk_mhz(dev.index or 0)
@@ -577,15 +687,7 @@ def main(argv=None) -> int:
               "bf16_peak_from_device_tflops": round(props.multi_processor_count * 4096 * max_mhz * 1e6 / 1e12, 1)
               if max_mhz else None,
               "sclk_under_load": sclk}
-    hbm = {}
-    for name, nbytes, s_, e_ in plan.hbm_ev:
-        d = hbm.setdefault(name, [0, 0.0, 0.0])
-        d[0] += 1
-        d[1] += s_.elapsed_time(e_)
-        d[2] += nbytes
-    hbm_kernels = [{"kernel": k, "calls": c, "bytes_per_call": b / c, "avg_ms": round(ms / c, 4),
-                    "GB/s": round(b / (ms * 1e-3) / 1e9, 1), "frac_of_hbm_peak": round(b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
-                   for k, (c, ms, b) in hbm.items()]
+    value, ms_step, ms_steps = m["value"], m["ms_step"], m["ms_steps"]
     result = {
         "metric": METRIC_BWD if bwd else METRIC,
         "value": round(value, 3),
@@ -601,27 +703,45 @@ def main(argv=None) -> int:
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic (seeded iid N(0,1), per-chunk generators)",
-        "config": {"workload": w.name + (f"_{args.mode}" if args.mode != "single" and w.kind in ("ring_share", "ulysses") else "")
-                   + ("_bwd" if bwd else "") + ("_graph" if graph is not None else ""),
-                   "batch": w.batch, "a2a": w.a2a, "zigzag": w.zigzag, "seq_len": w.seq_len, "cp_size": w.cp_size,
+        "config": {"workload": workload_name(w, args.mode, bwd, m["graph"]),
+                   "batch": w.batch, "a2a": w.a2a, "sharding": w.sharding, "seq_len": w.seq_len, "cp_size": w.cp_size,
                    "rank": w.rank, "group": w.group, "heads_q": w.heads_q, "heads_kv": w.heads_kv,
                    "head_dim": w.head_dim, "unmasked_flops_per_step": plan.flops},
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "kernel": kernel,
-                     "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4),
-                     "traffic": profiled_traffic(w.name, "block_fwd_bf16_kernel") if w.dtype == "bf16" and not bwd
+                     "achieved": round(m["achieved"], 3), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(m["achieved"] / peak, 4),
+                     "traffic": profiled_traffic(w.name, "block_fwd_bf16") if w.dtype == "bf16" and not bwd
                      else None,
-                     "avg_launch_ms": round(sum(attn_ms) / len(attn_ms), 4), "launches": len(attn_ms)},
-        "hbm_kernels": hbm_kernels,
+                     "avg_launch_ms": round(sum(m["attn_ms"]) / len(m["attn_ms"]), 4), "launches": len(m["attn_ms"])},
+        "hbm_kernels": m["hbm_kernels"],
+        "hbm_kernels_flushed": hbm_flushed(plan) if not args.no_flush else [],
         "device": device,
     }
     if bwd:
         result["cpu_baseline"] = None  # the oracle baseline is quoted for the forward line
     elif not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, plan.flops / (4.0 * w.head_dim))
+    if args.extras is None:
+        extras = EXTRAS if (args.workload == "ring_share_256k" and args.mode == "single" and not bwd
+                            and not args.graph) else []
+    else:
+        extras = [tuple(e.split(":")) if ":" in e else (e, "single") for e in args.extras.split(",") if e]
+    if extras:
+        del plan
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        result["extra"] = [extra_line(name, mode, args.steps, args.warmup, dev) for name, mode in extras]
     print(json.dumps(result), flush=True)
     return 0
+
+
+# Measured beside the default line, in the same run: the Ulysses group with the workload's
+# explicit permute, attention and inverse permute ("On Context Parallelism", All-to-all),
+# and the long-context ring share in its per-step form, one attention launch per ring step
+# into a tile and the merge kernel after each ("On Context Parallelism", Peer-to-peer /
+# Forward).
+EXTRAS = [("ulysses_gqa_128k", "single"), ("ring_share_256k", "unfused")]
 
 
 if __name__ == "__main__":

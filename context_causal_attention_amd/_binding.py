@@ -186,7 +186,7 @@ def block_fwd_rows(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_pos: tor
                    kv_pos: torch.Tensor, scale: float, out: torch.Tensor, lse: torch.Tensor | None = None):
     """cpattn_block_fwd_rows: bf16 block attention (batch 1) on row views.
 
-    q [Sq, Hq, 128], k, v [Skv, Hkv, 128] (bf16) and out [Sq, Hq, 128] (fp32) are views whose
+    q [Sq, Hq, D], k, v [Skv, Hkv, D] (bf16; D = 64 or 128) and out [Sq, Hq, D] (fp32) are views whose
     rows (dim 0) may be strided, e.g. one head group of a stacked buffer; within a row the
     heads and head dims are dense.  Writes out in place; returns (out, lse [1, Hq, Sq]).
     """
@@ -366,7 +366,7 @@ def ulysses_share_fwd(q_st: torch.Tensor, k_st: torch.Tensor, v_st: torch.Tensor
     output into the group's heads of ``out_st`` (fp32 [C, B, S/C, Hq, D]).
     Returns (out_grouped [B, S, Hq/C, D], lse [B, Hq/C, S]).
 
-    ``fused`` (default: whenever possible, i.e. B = 1, contiguous shards, bf16, D = 128): with
+    ``fused`` (default: whenever possible, i.e. B = 1, contiguous shards, bf16, D = 64 or 128): with
     one batch and contiguous shards, global row i of the group is row i of the stacked buffer
     at the group's head offset, so the attention reads Q, K, V in place and writes out_st
     directly (cpattn_block_fwd_rows), with the same bits as the explicit exchanges; out_grouped
@@ -374,7 +374,7 @@ def ulysses_share_fwd(q_st: torch.Tensor, k_st: torch.Tensor, v_st: torch.Tensor
     C, B, s, Hq, D = q_st.shape
     S = s * C
     if fused is None:
-        fused = (B == 1 and not zigzag and q_st.dtype == torch.bfloat16 and D == 128
+        fused = (B == 1 and not zigzag and q_st.dtype == torch.bfloat16 and D in (64, 128)
                  and all(t.is_contiguous() for t in (q_st, k_st, v_st, out_st)))
     if fused:
         Hkv = k_st.shape[3]

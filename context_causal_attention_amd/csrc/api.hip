@@ -86,13 +86,20 @@ CPATTN_API cpattn_status_t cpattn_zigzag_index_all(int64_t seq_len, int32_t cp_s
 
 namespace {
 
-// cpattn_block_fwd (merge = false) and cpattn_block_fwd_merge (merge = true) share their
-// validation and dispatch; `name` prefixes the error messages.
-cpattn_status_t block_fwd_common(const char* name, bool merge, const void* q, const void* k,
-                                 const void* v, cpattn_dtype_t dtype, int32_t batch, int64_t seq_q,
-                                 int64_t seq_kv, int32_t heads_q, int32_t heads_kv, int32_t head_dim,
-                                 const int64_t* q_positions, const int64_t* kv_positions, float scale,
-                                 float* out, float* lse, void* stream) {
+// The bf16 kernels form each lane's byte offset within a K/V (or Q) tile of up to 128 rows in
+// 32 bits: 127 rows times the row pitch must stay below 2^32 bytes, so a row (heads * head_dim
+// elements of 2 bytes) is bounded at 2^24 elements.
+constexpr int64_t kMaxRowElems = 1LL << 24;
+
+// Validation of one block attention call (cpattn_block_fwd, cpattn_block_fwd_merge and each
+// block of the fp32 ring share).  Returns CPATTN_OK when the call may launch; *empty is set
+// when there is nothing to launch (no query rows).  `name` prefixes the error messages.
+cpattn_status_t block_fwd_check(const char* name, const void* q, const void* k, const void* v,
+                                cpattn_dtype_t dtype, int32_t batch, int64_t seq_q, int64_t seq_kv,
+                                int32_t heads_q, int32_t heads_kv, int32_t head_dim,
+                                const int64_t* q_positions, const int64_t* kv_positions, float scale,
+                                float* out, float* lse, bool* empty) {
+    *empty = false;
     if (dtype != CPATTN_F32 && dtype != CPATTN_BF16)
         return fail(CPATTN_ERR_INVALID_ARG, "%s: unknown dtype %d", name, (int)dtype);
     if (batch <= 0 || heads_q <= 0 || heads_kv <= 0)
@@ -106,9 +113,13 @@ cpattn_status_t block_fwd_common(const char* name, bool merge, const void* q, co
                     heads_kv);
     if (head_dim != 64 && head_dim != 128)
         return fail(CPATTN_ERR_UNSUPPORTED, "%s: head_dim %d (supported: 64, 128)", name, head_dim);
-    if (dtype == CPATTN_BF16 && head_dim != 128)
-        return fail(CPATTN_ERR_UNSUPPORTED, "%s: bf16 path supports head_dim 128 only", name);
-    if (seq_q == 0) return ok();
+    if (dtype == CPATTN_BF16 && (int64_t)heads_kv * head_dim > kMaxRowElems)
+        return fail(CPATTN_ERR_UNSUPPORTED, "%s: heads_kv * head_dim = %lld above 2^24", name,
+                    (long long)heads_kv * head_dim);
+    if (seq_q == 0) {
+        *empty = true;
+        return ok();
+    }
     if (!q || !q_positions || !out || !lse)
         return fail(CPATTN_ERR_INVALID_ARG, "%s: q, q_positions, out and lse must be non-NULL", name);
     if (seq_kv > 0 && (!k || !v || !kv_positions))
@@ -122,6 +133,15 @@ cpattn_status_t block_fwd_common(const char* name, bool merge, const void* q, co
     // pq >= 32 query positions per block, so this bound holds for all of them
     if (dtype == CPATTN_BF16 && (seq_q + 31) / 32 * (int64_t)batch * heads_q > kMaxGrid)
         return fail(CPATTN_ERR_UNSUPPORTED, "%s: launch grid too large", name);
+    return ok();
+}
+
+// Launch of one validated block attention call.
+cpattn_status_t block_fwd_launch(const char* name, bool merge, const void* q, const void* k, const void* v,
+                                 cpattn_dtype_t dtype, int32_t batch, int64_t seq_q, int64_t seq_kv,
+                                 int32_t heads_q, int32_t heads_kv, int32_t head_dim,
+                                 const int64_t* q_positions, const int64_t* kv_positions, float scale,
+                                 float* out, float* lse, void* stream) {
     cpattn::BlockFwdArgs a{q,     k,      v,       q_positions, kv_positions, out,      lse,
                            batch, seq_q, seq_kv, heads_q,     heads_kv,     head_dim, scale, merge};
     a.n_blk = 1;
@@ -133,6 +153,20 @@ cpattn_status_t block_fwd_common(const char* name, bool merge, const void* q, co
     const hipError_t e = (dtype == CPATTN_BF16) ? cpattn::launch_block_fwd_bf16(a, (hipStream_t)stream)
                                                 : cpattn::launch_block_fwd_f32(a, (hipStream_t)stream);
     return from_hip(e, name);
+}
+
+// cpattn_block_fwd (merge = false) and cpattn_block_fwd_merge (merge = true).
+cpattn_status_t block_fwd_common(const char* name, bool merge, const void* q, const void* k,
+                                 const void* v, cpattn_dtype_t dtype, int32_t batch, int64_t seq_q,
+                                 int64_t seq_kv, int32_t heads_q, int32_t heads_kv, int32_t head_dim,
+                                 const int64_t* q_positions, const int64_t* kv_positions, float scale,
+                                 float* out, float* lse, void* stream) {
+    bool empty = false;
+    const cpattn_status_t st = block_fwd_check(name, q, k, v, dtype, batch, seq_q, seq_kv, heads_q, heads_kv,
+                                               head_dim, q_positions, kv_positions, scale, out, lse, &empty);
+    if (st != CPATTN_OK || empty) return st;
+    return block_fwd_launch(name, merge, q, k, v, dtype, batch, seq_q, seq_kv, heads_q, heads_kv, head_dim,
+                            q_positions, kv_positions, scale, out, lse, stream);
 }
 
 }  // namespace
@@ -170,7 +204,8 @@ CPATTN_API cpattn_status_t cpattn_block_fwd_rows(const void* q, int64_t q_row_st
         return fail(CPATTN_ERR_INVALID_ARG, "%s: scale must be finite and > 0", name);
     if (heads_q % heads_kv != 0)
         return fail(CPATTN_ERR_SHAPE, "%s: heads_q %d not a multiple of heads_kv %d", name, heads_q, heads_kv);
-    if (head_dim != 128) return fail(CPATTN_ERR_UNSUPPORTED, "%s: head_dim %d (supported: 128)", name, head_dim);
+    if (head_dim != 64 && head_dim != 128)
+        return fail(CPATTN_ERR_UNSUPPORTED, "%s: head_dim %d (supported: 64, 128)", name, head_dim);
     const int64_t qw = (int64_t)heads_q * head_dim, kw = (int64_t)heads_kv * head_dim;
     if (q_row_stride < qw || q_row_stride % 8 != 0 || q_row_stride > (1LL << 24) || kv_row_stride < kw ||
         kv_row_stride % 8 != 0 || kv_row_stride > (1LL << 24) || out_row_stride < qw || out_row_stride % 4 != 0)
@@ -246,6 +281,9 @@ CPATTN_API cpattn_status_t cpattn_block_bwd(const void* q, const void* k, const 
         return fail(CPATTN_ERR_UNSUPPORTED, "%s: head_dim %d (supported: 64, 128)", name, head_dim);
     if (dtype == CPATTN_BF16 && head_dim != 128)
         return fail(CPATTN_ERR_UNSUPPORTED, "%s: bf16 path supports head_dim 128 only", name);
+    if (dtype == CPATTN_BF16 && (int64_t)heads_q * head_dim > kMaxRowElems)
+        return fail(CPATTN_ERR_UNSUPPORTED, "%s: heads_q * head_dim = %lld above 2^24", name,
+                    (long long)heads_q * head_dim);
     if (seq_q == 0 || seq_kv == 0) {
         // no pair: nothing to add; accumulators to overwrite become zero
         if (wdq && seq_q > 0) {
@@ -294,12 +332,21 @@ CPATTN_API cpattn_status_t cpattn_ring_share_fwd(const void* q, const void* cons
     for (int32_t o = 0; o < n_blocks; ++o)
         if (seq_kv[o] < 0) return fail(CPATTN_ERR_INVALID_ARG, "%s: seq_kv[%d] < 0", name, o);
     if (dtype != CPATTN_BF16) {
-        // fp32: one block at a time, the later ones merged in the epilogue
+        // fp32: one block at a time, the later ones merged in the epilogue.  Every block is
+        // validated before the first launch, so a call that fails has enqueued nothing.
+        for (int32_t o = 0; o < n_blocks; ++o) {
+            bool empty = false;
+            const cpattn_status_t st =
+                block_fwd_check(name, q, k_blocks[o], v_blocks[o], dtype, batch, seq_q, seq_kv[o], heads_q,
+                                heads_kv, head_dim, q_positions, kv_positions[o], scale, out, lse, &empty);
+            if (st != CPATTN_OK) return st;
+            if (empty) return ok();  // no query rows: nothing to do for any block
+        }
         for (int32_t o = 0; o < n_blocks; ++o) {
             const cpattn_status_t st =
-                block_fwd_common(name, o > 0, q, k_blocks[o], v_blocks[o],
-                                 dtype, batch, seq_q, seq_kv[o], heads_q, heads_kv, head_dim, q_positions,
-                                 kv_positions[o], scale, out, lse, stream);
+                block_fwd_launch(name, o > 0, q, k_blocks[o], v_blocks[o], dtype, batch, seq_q, seq_kv[o],
+                                 heads_q, heads_kv, head_dim, q_positions, kv_positions[o], scale, out, lse,
+                                 stream);
             if (st != CPATTN_OK) return st;
         }
         return ok();
@@ -318,7 +365,11 @@ CPATTN_API cpattn_status_t cpattn_ring_share_fwd(const void* q, const void* cons
         return fail(CPATTN_ERR_INVALID_ARG, "%s: scale must be finite and > 0", name);
     if (heads_q % heads_kv != 0)
         return fail(CPATTN_ERR_SHAPE, "%s: heads_q %d not a multiple of heads_kv %d", name, heads_q, heads_kv);
-    if (head_dim != 128) return fail(CPATTN_ERR_UNSUPPORTED, "%s: bf16 path supports head_dim 128 only", name);
+    if (head_dim != 64 && head_dim != 128)
+        return fail(CPATTN_ERR_UNSUPPORTED, "%s: head_dim %d (supported: 64, 128)", name, head_dim);
+    if ((int64_t)heads_kv * head_dim > kMaxRowElems)
+        return fail(CPATTN_ERR_UNSUPPORTED, "%s: heads_kv * head_dim = %lld above 2^24", name,
+                    (long long)heads_kv * head_dim);
     if (seq_q == 0) return ok();
     if (!q || !q_positions || !out || !lse)
         return fail(CPATTN_ERR_INVALID_ARG, "%s: q, q_positions, out and lse must be non-NULL", name);

@@ -67,10 +67,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_AS __attribute__((address_space(3)))
 
-constexpr int kD = 128;             // head dim
 constexpr int kBN = 64;             // keys per tile
-constexpr int kRowBytes = kD * 2;   // one K/V row in LDS
-constexpr int kTileBytes = kBN * kRowBytes;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.0f;       // raise the running max only past this margin (log2)
@@ -104,7 +101,7 @@ struct Params {
     int32_t merge;     // merge into (out, lse) instead of overwriting them
     int32_t n_blk;     // K/V blocks attended in turn, as one softmax over all their keys
     int64_t q_rs;      // elements between consecutive rows of q, K/V and out (heads within a
-    int64_t kv_rs;     // row are contiguous: dense rows have heads * kD)
+    int64_t kv_rs;     // row are contiguous: dense rows have heads * D)
     int64_t out_rs;
     KVBlock blk[kMaxBlocks];
 };
@@ -135,6 +132,27 @@ __device__ inline bf16x8 lds_tr_pair(const LDS_AS char* p0, const LDS_AS char* p
     return __builtin_bit_cast(bf16x8, c);
 }
 
+// Head-dim dependent layout of a K/V tile in LDS: one row of D bf16 is D/8 chunks of 16 bytes,
+// and chunk c of row r is stored at chunk c ^ swz(r).
+//   K (row reads: 16 lanes read one chunk of 16 consecutive keys, which must fall in 16
+//   distinct 16-byte bank groups of the 256-byte bank row):
+//     D = 128 (one row per bank row): r & 15
+//     D = 64 (two rows per bank row): (r >> 1) & 7
+//   V (transposed reads: each 32-lane half reads 4 consecutive keys x 4 chunks, which must
+//   cover all 64 banks):
+//     D = 128: (r & 3) << 2
+//     D = 64: ((r >> 1) & 1) << 2
+// Both are unchanged by adding a multiple of 8 rows, which the operand reads rely on.
+template <int D> struct TileGeom {
+    static_assert(D == 64 || D == 128, "head dim 64 or 128");
+    static constexpr int kRowBytes = D * 2;
+    static constexpr int kTileBytes = kBN * kRowBytes;
+    static constexpr int kChunks = D / 8;             // 16-byte chunks per row
+    static constexpr int kRowsPerLoad = 64 / kChunks; // rows one 64-lane 16-byte load fills
+    __device__ static inline int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+    __device__ static inline int swz_v(int r) { return D == 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2); }
+};
+
 // Buffer descriptor over `bytes` bytes from `base` (raw, no stride; word 3 as gfx9 wants).
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
@@ -153,16 +171,17 @@ constexpr int kReadAheadK = 4;
 constexpr int kReadAheadV = 2;
 constexpr int kReadAheadK2 = 2;
 
-template <int NW, int NB, int KBP, int KS>
+template <int D, int NW, int NB, int KBP, int KS>
 __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params p) {
     static_assert(KS == 1 || NB == 1, "the key split combines one column block per wave");
+    using TG = TileGeom<D>;
+    constexpr int kD = D;
+    constexpr int kRowBytes = TG::kRowBytes;
+    constexpr int kTileBytes = TG::kTileBytes;
     constexpr int kRAK = KBP == 1 ? kReadAheadK2 : kReadAheadK;
     constexpr int kThreads = 64 * NW;
     constexpr int NWR = NW / KS;  // waves per row group (all waves unless the keys are split)
-    // K/V tile row r, 16-byte chunk c is stored at chunk c ^ swz(r):
-    //   K: r & 15 (row reads by 16 consecutive keys are conflict-free)
-    //   V: (r & 3) << 2 (transposed reads: each 32-lane half reads 4 consecutive keys x 64 B,
-    //      which this spreads over all 64 banks)
+    // K/V tile row r, 16-byte chunk c is stored at chunk c ^ swz(r) (TileGeom);
     // two stages in two distinct arrays, so that the compiler can tell the stage being read
     // from the stage being filled and does not wait for the fill before reading
     // (with the keys split over KS wave groups, each group has its own pair of stages)
@@ -236,8 +255,9 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
     int n_total = 0;  // tiles over all blocks
     for (int o = 0; o < p.n_blk; ++o) n_total += blk_ne[o];
 
-    // ---- K/V tile loads: each wave fills (64 / NW) rows of K and of V per tile, four rows
-    // (1 KB) per instruction; lane -> row (lane >> 4), stored chunk (lane & 15).  The source
+    // ---- K/V tile loads: each wave fills (64 / NW) rows of K and of V per tile, 1 KB (four
+    // rows of D = 128, eight of D = 64) per instruction; lane -> row (lane / chunks per row),
+    // stored chunk (lane % chunks per row).  The source
     // address is a wave-uniform tile base plus a per-lane byte offset fixed for the kernel;
     // only a ragged last tile clamps its rows (to the last key, finite data the mask hides).
     const int64_t kvstride = p.kv_rs;  // elements between consecutive keys
@@ -250,24 +270,66 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
     };
     constexpr int kLW = NWR < 8 ? NWR : 8;  // waves of a row group that load (all, or the first 8)
     constexpr int kRowsPerWave = kBN / kLW;
-    constexpr int kLoadsPerWave = kRowsPerWave / 4;
-    const int ld_row_in = lane >> 4;   // row within the 4-row slab
-    const int ld_chunk = lane & 15;    // stored chunk
+    constexpr int kRPL = TG::kRowsPerLoad;
+    static_assert(kRowsPerWave % kRPL == 0, "whole loads per wave");
+    constexpr int kLoadsPerWave = kRowsPerWave / kRPL;
+    const int ld_row_in = lane / TG::kChunks;   // row within the slab of one load
+    const int ld_chunk = lane % TG::kChunks;    // stored chunk
     uint32_t koff[kLoadsPerWave], voff[kLoadsPerWave];
 #pragma unroll
     for (int i = 0; i < kLoadsPerWave; ++i) {
-        const int row = wr * kRowsPerWave + 4 * i + ld_row_in;
-        koff[i] = (uint32_t)(row * kvstride * 2) + ((ld_chunk ^ (row & 15)) << 4);
-        voff[i] = (uint32_t)(row * kvstride * 2) + ((ld_chunk ^ ((row & 3) << 2)) << 4);
+        const int row = wr * kRowsPerWave + kRPL * i + ld_row_in;
+        koff[i] = (uint32_t)(row * kvstride * 2) + ((ld_chunk ^ TG::swz_k(row)) << 4);
+        voff[i] = (uint32_t)(row * kvstride * 2) + ((ld_chunk ^ TG::swz_v(row)) << 4);
     }
-    // tile jt of block o into the stage at kt
-    auto issue_tile = [&](int o, int jt, LDS_AS char* kt) {
+    // cursors: the tile being computed (block oc, tile jt of its ne_c visible tiles; n_full
+    // of oc) and the next one to load (block on, tile jn of ne_n, the tile's K and V
+    // addresses and the block's length; on == p.n_blk when there is none).  All are uniform
+    // and live in scalar registers: a step within a block only counts and adds, and the
+    // per-block counts (LDS) and addresses (kernel arguments) are read when a cursor enters
+    // a new block, so no memory round trip sits between a barrier and the next tile.
+    int oc = 0, jt = 0, ne_c = 0, n_full = 0;
+    int on = p.n_blk, jn = 0, ne_n = 0;  // no load until set_load (a key group may have no tile)
+    const char* kb_n = nullptr;
+    const char* vb_n = nullptr;
+    int64_t seq_n = 0;
+    auto ne_of = [&](int o) { return o < p.n_blk ? __builtin_amdgcn_readfirstlane(blk_ne[o]) : 0; };
+    auto next_block = [&](int o) {
+        do { ++o; } while (o < p.n_blk && blk_ne[o] == 0);
+        return o;
+    };
+    auto set_load = [&](int o, int j) {
+        on = o;
+        jn = j;
+        ne_n = ne_of(o);
+        if (o < p.n_blk) {
+            kb_n = kbase_of(o) + (int64_t)j * tile_bytes_g;
+            vb_n = vbase_of(o) + (int64_t)j * tile_bytes_g;
+            seq_n = p.blk[o].seq;
+        }
+    };
+    auto adv_c = [&]() {
+        if (++jt >= ne_c) {
+            jt = 0;
+            oc = next_block(oc);
+            ne_c = ne_of(oc);
+        }
+    };
+    auto adv_n = [&]() {
+        kb_n += tile_bytes_g;
+        vb_n += tile_bytes_g;
+        if (++jn >= ne_n) set_load(next_block(on), 0);
+    };
+    // the load cursor's tile into the stage at kt
+    auto issue_tile = [&](LDS_AS char* kt) {
         LDS_AS char* vt = kt + kTileBytes;
-        const char* kb_t = kbase_of(o) + (int64_t)jt * tile_bytes_g;
-        const char* vb_t = vbase_of(o) + (int64_t)jt * tile_bytes_g;
-        const int64_t seq_o = p.blk[o].seq;
+        const char* kb_t = kb_n;
+        const char* vb_t = vb_n;
+        const int64_t seq_o = seq_n;
+        const int jt = jn;
         // the descriptor covers this tile's rows that exist (a tile spans < 4 GiB)
         const int64_t rows = seq_o - (int64_t)jt * kBN < kBN ? seq_o - (int64_t)jt * kBN : kBN;
+        if (rows <= 0) return;  // never a tile without rows (the cursor stays within its block)
         const uint32_t span = (uint32_t)((rows - 1) * kvstride * 2 + kRowBytes);
         const __amdgpu_buffer_rsrc_t kr = make_rsrc(kb_t, span);
         const __amdgpu_buffer_rsrc_t vr = make_rsrc(vb_t, span);
@@ -275,17 +337,17 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
         if ((int64_t)(jt + 1) * kBN <= seq_o) {
 #pragma unroll
             for (int i = 0; i < kLoadsPerWave; ++i) {
-                load_lds16(kr, koff[i], kt + (wr * kRowsPerWave + 4 * i) * kRowBytes);
-                load_lds16(vr, voff[i], vt + (wr * kRowsPerWave + 4 * i) * kRowBytes);
+                load_lds16(kr, koff[i], kt + (wr * kRowsPerWave + kRPL * i) * kRowBytes);
+                load_lds16(vr, voff[i], vt + (wr * kRowsPerWave + kRPL * i) * kRowBytes);
             }
         } else {
 #pragma unroll
             for (int i = 0; i < kLoadsPerWave; ++i) {
-                const int row = wr * kRowsPerWave + 4 * i + ld_row_in;
+                const int row = wr * kRowsPerWave + kRPL * i + ld_row_in;
                 const int64_t j = (int64_t)jt * kBN + row;
                 const uint32_t over = (j >= seq_o) ? (uint32_t)((j - (seq_o - 1)) * kvstride * 2) : 0u;
-                load_lds16(kr, koff[i] - over, kt + (wr * kRowsPerWave + 4 * i) * kRowBytes);
-                load_lds16(vr, voff[i] - over, vt + (wr * kRowsPerWave + 4 * i) * kRowBytes);
+                load_lds16(kr, koff[i] - over, kt + (wr * kRowsPerWave + kRPL * i) * kRowBytes);
+                load_lds16(vr, voff[i] - over, vt + (wr * kRowsPerWave + kRPL * i) * kRowBytes);
             }
         }
     };
@@ -347,16 +409,16 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
     }
 
     // ---- per-lane LDS read offsets
-    // K (row reads): key = 32*kb + l32, chunk (2*ks + half) stored at chunk ^ (key & 15)
+    // K (row reads): key = 32*kb + l32, chunk (2*ks + half) stored at chunk ^ swz_k(key)
     uint32_t off_k[kD / 16];
 #pragma unroll
     for (int ks = 0; ks < kD / 16; ++ks)
-        off_k[ks] = l32 * kRowBytes + (((2 * ks + half) ^ (lane & 15)) << 4);
+        off_k[ks] = l32 * kRowBytes + (((2 * ks + half) ^ TG::swz_k(l32)) << 4);
     // V (transposed reads): in each 16-lane group, lane s reads 4 dims starting at
     // 16*(group&1) + 4*(s&3) of key (s>>2) + 4*half (+8 for the second read)
     const int grp = lane >> 4, s16 = lane & 15;
     const int vkey = 4 * half + (s16 >> 2);
-    const int vsw = (vkey & 3) << 2;
+    const int vsw = TG::swz_v(vkey);
     uint32_t off_v[kD / 32];
 #pragma unroll
     for (int db = 0; db < kD / 32; ++db) {
@@ -367,16 +429,6 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
     LDS_AS char* st0 = (LDS_AS char*)lds_stage0 + ksg * 2 * kTileBytes;
     LDS_AS char* st1 = (LDS_AS char*)lds_stage1 + ksg * 2 * kTileBytes;
 
-    // cursors: the tile being computed (block oc, tile jt; n_full of oc) and the next one to
-    // load (block on, tile jn; on == p.n_blk when there is none)
-    int oc = 0, jt = 0, n_full = 0;
-    int on = 0, jn = 0;
-    auto advance = [&](int& o, int& j) {
-        if (++j >= blk_ne[o]) {
-            j = 0;
-            do { ++o; } while (o < p.n_blk && blk_ne[o] == 0);
-        }
-    };
     // one tile: prefetch the next tile into `nxt`, compute the current one from `cur`
     auto tile = [&](const LDS_AS char* kt, LDS_AS char* nxt) {
         const LDS_AS char* vt = kt + kTileBytes;
@@ -384,13 +436,13 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
         // between the passes: right after the barrier all twelve waves start their score
         // products at once, and issuing the loads there too slowed the kernel (between the
         // passes: +2-4%, the loads still land within the second pass).
-        if (KBP != 1 && on < p.n_blk) issue_tile(on, jn, nxt);
+        if (KBP != 1 && on < p.n_blk) issue_tile(nxt);
 
         // the tile in 2 / KBP passes of 32 * KBP keys each: scores, mask, softmax, PV (with the
         // keys split, a group whose share has run out only keeps the barriers)
 #pragma unroll
         for (int ps = 0; ps < ((KS == 1 || oc < p.n_blk) ? 2 / KBP : 0); ++ps) {
-            if (KBP == 1 && ps == 1 && on < p.n_blk) issue_tile(on, jn, nxt);
+            if (KBP == 1 && ps == 1 && on < p.n_blk) issue_tile(nxt);
             // S^T = K Q^T
             f32x16 s[NB][KBP];
 #pragma unroll
@@ -410,7 +462,7 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
             // keep the operand reads kRAK ahead of the matrix products
             __builtin_amdgcn_sched_group_barrier(0x100, kRAK, 1);
 #pragma unroll
-            for (int i = 0; i < 8 * KBP - kRAK; ++i) {
+            for (int i = 0; i < (kD / 16) * KBP - kRAK; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, NB, 1);
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
             }
@@ -500,7 +552,7 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
             }
             __builtin_amdgcn_sched_group_barrier(0x100, 2 * kReadAheadV, 2);
 #pragma unroll
-            for (int i = 0; i < 8 * KBP - kReadAheadV; ++i) {
+            for (int i = 0; i < (kD / 16) * KBP - kReadAheadV; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, NB, 2);
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
             }
@@ -511,37 +563,37 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
         __syncthreads();
         const int o_prev = oc;
         if (KS == 1) {
-            advance(oc, jt);
-            if (on < p.n_blk) advance(on, jn);
+            adv_c();
+            if (on < p.n_blk) adv_n();
         } else {
 #pragma unroll
             for (int s2 = 0; s2 < KS; ++s2) {
-                if (oc < p.n_blk) advance(oc, jt);
-                if (on < p.n_blk) advance(on, jn);
+                if (oc < p.n_blk) adv_c();
+                if (on < p.n_blk) adv_n();
             }
         }
         if (oc != o_prev && oc < p.n_blk) {
-            n_full = blk_full[oc];
+            n_full = __builtin_amdgcn_readfirstlane(blk_full[oc]);
             find_vis(oc);
         }
     };
 
     while (oc < p.n_blk && blk_ne[oc] == 0) ++oc;  // first block with a visible tile
+    ne_c = ne_of(oc);
     // key group g starts at tile g of the sequence
     for (int s2 = 0; s2 < ksg; ++s2)
-        if (oc < p.n_blk) advance(oc, jt);
+        if (oc < p.n_blk) adv_c();
     if (oc < p.n_blk) {
-        n_full = blk_full[oc];
+        n_full = __builtin_amdgcn_readfirstlane(blk_full[oc]);
         find_vis(oc);
-        issue_tile(oc, jt, st0);
-        on = oc;
-        jn = jt;
+        set_load(oc, jt);
+        issue_tile(st0);
         if (KS == 1) {
-            advance(on, jn);
+            adv_n();
         } else {
 #pragma unroll
             for (int s2 = 0; s2 < KS; ++s2)
-                if (on < p.n_blk) advance(on, jn);
+                if (on < p.n_blk) adv_n();
         }
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), visible to the compiler
@@ -625,13 +677,31 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
     }
 }
 
-template <int NW, int NB, int KBP, int KS>
+template <int D, int NW, int NB, int KBP, int KS>
 hipError_t launch_variant(Params p, int64_t seq_q, hipStream_t stream) {
     p.pq = 32 * (NW / KS) * NB / p.G;
     p.n_qt = (seq_q + p.pq - 1) / p.pq;
     const int64_t blocks = p.n_qt * p.n_cols;
-    hipLaunchKernelGGL((block_fwd_bf16_kernel<NW, NB, KBP, KS>), dim3((unsigned)blocks), dim3(64 * NW), 0, stream, p);
+    hipLaunchKernelGGL((block_fwd_bf16_kernel<D, NW, NB, KBP, KS>), dim3((unsigned)blocks), dim3(64 * NW), 0, stream, p);
     return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_head_dim(const BlockFwdArgs& a, Params p, hipStream_t stream) {
+    // When 8-wave blocks would leave the chip less than half full: 8 waves over 128 rows with
+    // the keys split between two wave groups (two waves per SIMD on every CU, where plain
+    // 4-wave blocks would have one).  Otherwise 12 waves (three per SIMD: more of each wave's
+    // softmax runs under the other waves' products; +5-7% on causal launches) when the
+    // blocks' work differs, i.e. the launch walks several K/V blocks or the queries and keys
+    // share one positions array (a causal triangle): the heavy blocks run first, so the last
+    // round of blocks is light.  Launches of equal-work blocks (queries against another
+    // shard's keys) keep 8 waves: 12-wave blocks hold 384/G positions (96 for G = 4), which
+    // split a power-of-two shard into a part-filled last round of the 256 CUs, while
+    // 64-position blocks divide it evenly.
+    const int64_t blocks8 = ((a.seq_q + 256 / p.G - 1) / (256 / p.G)) * p.n_cols;
+    if (blocks8 < 512) return launch_variant<D, 8, 1, 2, 2>(p, a.seq_q, stream);
+    if (a.n_blk > 1 || a.blk[0].pos == a.q_pos) return launch_variant<D, 12, 1, 1, 1>(p, a.seq_q, stream);
+    return launch_variant<D, 8, 1, 2, 1>(p, a.seq_q, stream);
 }
 
 }  // namespace
@@ -644,9 +714,9 @@ hipError_t launch_block_fwd_bf16(const BlockFwdArgs& a, hipStream_t stream) {
     p.lse = a.lse;
     p.seq_q = a.seq_q;
     p.n_blk = a.n_blk;
-    p.q_rs = a.q_row_stride > 0 ? a.q_row_stride : (int64_t)a.heads_q * kD;
-    p.kv_rs = a.kv_row_stride > 0 ? a.kv_row_stride : (int64_t)a.heads_kv * kD;
-    p.out_rs = a.out_row_stride > 0 ? a.out_row_stride : (int64_t)a.heads_q * kD;
+    p.q_rs = a.q_row_stride > 0 ? a.q_row_stride : (int64_t)a.heads_q * a.head_dim;
+    p.kv_rs = a.kv_row_stride > 0 ? a.kv_row_stride : (int64_t)a.heads_kv * a.head_dim;
+    p.out_rs = a.out_row_stride > 0 ? a.out_row_stride : (int64_t)a.heads_q * a.head_dim;
     for (int o = 0; o < a.n_blk; ++o)
         p.blk[o] = KVBlock{(const __bf16*)a.blk[o].k, (const __bf16*)a.blk[o].v, a.blk[o].pos, a.blk[o].seq};
     p.heads_q = a.heads_q;
@@ -658,20 +728,7 @@ hipError_t launch_block_fwd_bf16(const BlockFwdArgs& a, hipStream_t stream) {
     p.xcd_cols = (p.n_cols % 8 == 0) ? p.n_cols / 8 : 0;
     p.c = a.scale * kLog2e;
     p.merge = a.merge ? 1 : 0;
-    // When 8-wave blocks would leave the chip less than half full: 8 waves over 128 rows with
-    // the keys split between two wave groups (two waves per SIMD on every CU, where plain
-    // 4-wave blocks would have one).  Otherwise 12 waves (three per SIMD: more of each wave's
-    // softmax runs under the other waves' products; +5-7% on causal launches) when the
-    // blocks' work differs, i.e. the launch walks several K/V blocks or the queries and keys
-    // share one positions array (a causal triangle): the heavy blocks run first, so the last
-    // round of blocks is light.  Launches of equal-work blocks (queries against another
-    // shard's keys) keep 8 waves: 12-wave blocks hold 384/G positions (96 for G = 4), which
-    // split a power-of-two shard into a part-filled last round of the 256 CUs, while
-    // 64-position blocks divide it evenly.
-    const int64_t blocks8 = ((a.seq_q + 256 / p.G - 1) / (256 / p.G)) * p.n_cols;
-    if (blocks8 < 512) return launch_variant<8, 1, 2, 2>(p, a.seq_q, stream);
-    if (a.n_blk > 1 || a.blk[0].pos == a.q_pos) return launch_variant<12, 1, 1, 1>(p, a.seq_q, stream);
-    return launch_variant<8, 1, 2, 1>(p, a.seq_q, stream);
+    return a.head_dim == 64 ? launch_head_dim<64>(a, p, stream) : launch_head_dim<128>(a, p, stream);
 }
 
 }  // namespace cpattn

@@ -35,6 +35,15 @@ class Workload:
         return self.seq_len // (2 * self.cp_size)
 
     @property
+    def sharding(self) -> str:
+        """How the sequence is split over the C ranks: zigzag (rank r owns chunks r and
+        2C-1-r) for the ring, all-gather and mesh shares and the zigzag Ulysses workload;
+        contiguous (rank r owns [r*S/C, (r+1)*S/C)) for the plain Ulysses workload."""
+        if self.kind == "ulysses" and not self.zigzag:
+            return "contiguous"
+        return "zigzag"
+
+    @property
     def local_len(self) -> int:
         return self.seq_len // self.cp_size
 

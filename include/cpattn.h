@@ -124,10 +124,13 @@ cpattn_status_t cpattn_zigzag_index_all(int64_t seq_len, int32_t cp_size, int64_
  * dtype CPATTN_BF16: bf16 inputs, products accumulated in fp32 on the matrix cores; the
  * softmax weights are rounded to bf16 (round to nearest even) before the second product;
  * the row sums are kept in fp32.  dtype CPATTN_F32: fp32 throughout.
- * head_dim must be 64 or 128.  seq_q == 0 is a no-op (pointers may be NULL); seq_kv == 0
- * writes out = 0, lse = -inf (k, v, kv_positions may be NULL).
+ * head_dim must be 64 or 128, for both dtypes.  seq_q == 0 is a no-op (pointers may be
+ * NULL); seq_kv == 0 writes out = 0, lse = -inf (k, v, kv_positions may be NULL).
+ * bf16: q, k, v, out 16-byte aligned, and a K/V row (heads_kv * head_dim elements) at most
+ * 2^24 elements, since the kernels form offsets within a tile of rows in 32 bits.
  * Errors: INVALID_ARG (NULL pointer, batch/heads <= 0, seq < 0, bad scale or dtype),
- * SHAPE (heads_q % heads_kv != 0), UNSUPPORTED (head_dim not 64/128).
+ * SHAPE (heads_q % heads_kv != 0), UNSUPPORTED (head_dim not 64/128, misalignment, a K/V
+ * row above 2^24 elements, a launch grid too large).
  */
 cpattn_status_t cpattn_block_fwd(const void* q, const void* k, const void* v, cpattn_dtype_t dtype,
                                  int32_t batch, int64_t seq_q, int64_t seq_kv, int32_t heads_q,
@@ -164,10 +167,10 @@ cpattn_status_t cpattn_block_fwd_merge(const void* q, const void* k, const void*
                                        float* lse, void* stream);
 
 /*
- * cpattn_block_fwd_rows -- cpattn_block_fwd (bf16, batch 1, head_dim 128) on strided rows:
- * q, k, v and out are sequences of rows whose consecutive rows lie q_row_stride,
+ * cpattn_block_fwd_rows -- cpattn_block_fwd (bf16, batch 1, head_dim 64 or 128) on strided
+ * rows: q, k, v and out are sequences of rows whose consecutive rows lie q_row_stride,
  * kv_row_stride and out_row_stride elements apart; within a row the heads are contiguous
- * (head h at h * 128).  This lets Ulysses' head group be read in place from the stacked
+ * (head h at h * head_dim; the lines below write 128 for head_dim).  This lets Ulysses' head group be read in place from the stacked
  * rank shards and its output written back into them: with B = 1 and contiguous shards,
  * the exchange of [HB] "Ulysses" / [OLMO] Eq. (96) maps global row i of group g to row i
  * of the stacked buffer at head offset g * H/C, so q = Q_st + g*(Hq/C)*128 with
@@ -184,7 +187,7 @@ cpattn_status_t cpattn_block_fwd_merge(const void* q, const void* k, const void*
  * seq_q == 0 is a no-op; seq_kv == 0 gives out = 0 and lse = -inf (k, v, kv_positions may
  * then be NULL).  Pointers 16-byte aligned.
  * Errors: INVALID_ARG (NULL pointer, heads <= 0, seq < 0, bad scale), SHAPE (heads_q %
- * heads_kv != 0), UNSUPPORTED (head_dim != 128, a stride too small, too large or not a
+ * heads_kv != 0), UNSUPPORTED (head_dim not 64/128, a stride too small, too large or not a
  * multiple of its unit, misalignment).
  */
 cpattn_status_t cpattn_block_fwd_rows(const void* q, int64_t q_row_stride, const void* k,
@@ -210,10 +213,11 @@ cpattn_status_t cpattn_block_fwd_rows(const void* q, int64_t q_row_stride, const
  *                        each strictly increasing
  *   seq_kv               host array of n_blocks lengths (0: the block is skipped)
  *   n_blocks             1 .. 16
- * dtype CPATTN_BF16: one launch (head_dim 128).  CPATTN_F32: cpattn_block_fwd on the first
- * block and cpattn_block_fwd_merge on the others.
+ * dtype CPATTN_BF16: one launch (head_dim 64 or 128).  CPATTN_F32: cpattn_block_fwd on the
+ * first block and cpattn_block_fwd_merge on the others; every block is validated before
+ * the first of them is launched.
  * Errors: as for cpattn_block_fwd, and INVALID_ARG for n_blocks outside [1, 16] or NULL
- * arrays.
+ * arrays.  A call that returns an error has enqueued nothing, for either dtype.
  */
 cpattn_status_t cpattn_ring_share_fwd(const void* q, const void* const* k_blocks,
                                       const void* const* v_blocks, const int64_t* const* kv_positions,
@@ -286,7 +290,8 @@ cpattn_status_t cpattn_attn_bwd_delta(const float* out, const void* dout, cpattn
  *                WRITE_DQ on its first step, so no accumulator needs clearing.
  * dtype CPATTN_BF16: bf16 products with fp32 accumulation; p and ds are rounded to bf16
  * (RNE) before the products that use them.  CPATTN_F32: fp32 throughout.  head_dim 64 or
- * 128 (bf16: 128).  seq_q == 0 or seq_kv == 0 adds nothing.
+ * 128 (bf16: 128, and a Q row of heads_q * 128 elements at most 2^24).  seq_q == 0 or
+ * seq_kv == 0 adds nothing.
  * Errors: INVALID_ARG (also unknown flag bits), SHAPE, UNSUPPORTED as for cpattn_block_fwd.
  */
 cpattn_status_t cpattn_block_bwd(const void* q, const void* k, const void* v, const void* dout,

@@ -77,7 +77,16 @@ def test_block_fwd_validation(lib):
     assert _bf(lib, scale=float("nan")) == INVALID
     assert _bf(lib, hq=6, hkv=4) == SHAPE and "multiple" in _err(lib)
     assert _bf(lib, d=96) == UNSUPPORTED
-    assert _bf(lib, d=64, dtype=1) == UNSUPPORTED  # bf16 path is D=128 only
+    # bf16 takes D = 64 as well as 128: such a call gets past the head-dim check to the
+    # pointer checks
+    assert _bf(lib, d=64, dtype=1, q=NULL) == INVALID
+    # the bf16 kernels form tile offsets in 32 bits: a K/V row of more than 2^24 elements is
+    # refused, whatever the head dim
+    assert _bf(lib, hq=(1 << 17) + 1, hkv=(1 << 17) + 1, d=128) == UNSUPPORTED and "2^24" in _err(lib)
+    assert _bf(lib, hq=(1 << 18) + 1, hkv=(1 << 18) + 1, d=64) == UNSUPPORTED and "2^24" in _err(lib)
+    assert _bf(lib, hq=(1 << 18), hkv=(1 << 18), d=64, q=NULL) == INVALID  # 2^24 exactly is allowed
+    # the fp32 path has no such bound
+    assert _bf(lib, hq=(1 << 17) + 1, hkv=(1 << 17) + 1, d=128, dtype=0, q=NULL) == INVALID
     assert _bf(lib, q=NULL) == INVALID
     assert _bf(lib, out=NULL) == INVALID
     assert _bf(lib, kvpos=NULL) == INVALID
@@ -141,7 +150,9 @@ def test_block_fwd_merge_validation(lib):
     assert bfm(batch=0) == INVALID
     assert bfm(scale=float("nan")) == INVALID
     assert bfm(hq=6, hkv=4) == SHAPE
-    assert bfm(d=64, dtype=1) == UNSUPPORTED
+    assert bfm(d=96, dtype=1) == UNSUPPORTED
+    assert bfm(d=64, dtype=1, q=NULL) == INVALID  # D = 64 gets past the head-dim check
+    assert bfm(hq=(1 << 17) + 1, hkv=(1 << 17) + 1) == UNSUPPORTED and "2^24" in _err(lib)
     assert bfm(lse=NULL) == INVALID
     assert bfm(out=ctypes.c_void_p(0x1004)) == UNSUPPORTED
     assert bfm(seq_q=0, q=NULL, out=NULL, lse=NULL, qpos=NULL) == OK
@@ -203,7 +214,9 @@ def test_block_bwd_validation(lib):
     assert _bb(lib, scale=float("nan")) == INVALID
     assert _bb(lib, hq=6, hkv=4) == SHAPE and "multiple" in _err(lib)
     assert _bb(lib, d=96, dtype=0) == UNSUPPORTED
-    assert _bb(lib, d=64, dtype=1) == UNSUPPORTED  # bf16 path is D=128 only
+    assert _bb(lib, d=64, dtype=1) == UNSUPPORTED  # bf16 backward is D=128 only
+    # bf16 rows of Q (heads_q * head_dim) above 2^24 elements are refused
+    assert _bb(lib, hq=(1 << 17) + 2, hkv=2) == UNSUPPORTED and "2^24" in _err(lib)
     for name in ("q", "k", "v", "dout", "qpos", "kvpos", "lse", "delta", "dq", "dk", "dv"):
         assert _bb(lib, **{name: NULL}) == INVALID, name
     for name in ("q", "k", "v", "dout", "dq", "dk", "dv"):
@@ -244,7 +257,9 @@ def test_ring_share_fwd_validation(lib):
     assert _rs(lib, seq_q=-1) == INVALID
     assert _rs(lib, scale=float("inf")) == INVALID
     assert _rs(lib, hq=6, hkv=4) == SHAPE
-    assert _rs(lib, d=64) == UNSUPPORTED
+    assert _rs(lib, d=96) == UNSUPPORTED
+    assert _rs(lib, d=64, q=NULL) == INVALID  # bf16 D = 64 gets past the head-dim check
+    assert _rs(lib, hq=(1 << 17) + 1, hkv=(1 << 17) + 1) == UNSUPPORTED and "2^24" in _err(lib)
     for name in ("q", "qpos", "out", "lse"):
         assert _rs(lib, **{name: NULL}) == INVALID, name
     assert _rs(lib, q=ctypes.c_void_p(0x1004)) == UNSUPPORTED
@@ -253,6 +268,10 @@ def test_ring_share_fwd_validation(lib):
     # the fp32 path checks each block as a single-block call does
     assert _rs(lib, dtype=0, d=96) == UNSUPPORTED
     assert _rs(lib, dtype=0, hq=6, hkv=4) == SHAPE
+    # ... and every block before the first launch: a bad later block fails the call with
+    # nothing enqueued (without a GPU, a launch would have returned CPATTN_ERR_HIP instead)
+    assert _rs(lib, dtype=0, ks=[0x1000, 0, 0x1000, 0x1000]) == INVALID
+    assert _rs(lib, dtype=0, ps=[0x1000, 0x1000, 0x1000, 0]) == INVALID
 
 
 def _rows(lib, **kw):
@@ -268,7 +287,8 @@ def test_block_fwd_rows_validation(lib):
     assert _rows(lib, sq=-1) == INVALID
     assert _rows(lib, scale=float("nan")) == INVALID
     assert _rows(lib, hq=6, hkv=4, qs=768, ks=512, os=768) == SHAPE
-    assert _rows(lib, d=64) == UNSUPPORTED
+    assert _rows(lib, d=96) == UNSUPPORTED
+    assert _rows(lib, d=64, qs=256, ks=64, os=256, q=NULL) == INVALID  # D = 64 gets past the head-dim check
     # row strides: at least a row, multiples of 8 (q, k/v) or 4 (out), q and k/v at most 2^24
     assert _rows(lib, qs=504) == UNSUPPORTED and "row strides" in _err(lib)
     assert _rows(lib, ks=120) == UNSUPPORTED

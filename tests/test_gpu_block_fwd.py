@@ -271,3 +271,65 @@ def test_block_fwd_rows_no_keys():
     torch.cuda.synchronize()
     assert torch.count_nonzero(out[:, 8:]) == 0 and bool((out[:, :8] == 5.0).all())
     assert bool(torch.isneginf(lse).all())
+
+
+# bf16 with head dim 64: the same kernels instantiated for 128-byte rows (their own LDS
+# swizzles), small launches (keys split over two wave groups) and launch sizes (the
+# software-pipelined kernel)
+@pytest.mark.parametrize("case", [(1, 256, 256, 2, 2), (2, 200, 333, 4, 2), (1, 97, 300, 6, 2), (3, 45, 513, 8, 4)])
+def test_bf16_head_dim_64_small(case):
+    B, Sq, Skv, Hq, Hkv = case
+    q, k, v = _inputs(64 + Sq, B, Sq, Skv, Hq, Hkv, 64, torch.bfloat16)
+    kvpos = np.arange(Skv, dtype=np.int64)
+    qpos = np.arange(Skv - Sq, Skv, dtype=np.int64) if Sq <= Skv else np.arange(Sq, dtype=np.int64)
+    _run_and_compare(q, k, v, qpos, kvpos, 0.125, "bf16")
+
+
+def test_bf16_head_dim_64_zigzag_steps():
+    C, t, Hq, Hkv = 4, 96, 4, 2
+    S = 2 * C * t
+    q, _, _ = _inputs(640, 1, S // C, 1, Hq, Hkv, 64, torch.bfloat16)
+    for r in (0, C - 1):
+        for o in range(C):
+            _, k, v = _inputs(650 + o, 1, 1, S // C, Hq, Hkv, 64, torch.bfloat16)
+            _run_and_compare(q, k, v, oracle.zigzag_positions(S, C, r), oracle.zigzag_positions(S, C, o), 0.125,
+                             "bf16")
+
+
+@pytest.mark.parametrize("case", [(1, 6000, 32, 8), (2, 4100, 16, 4)])
+def test_bf16_head_dim_64_large(case):
+    B, S, Hq, Hkv = case
+    D = 64
+    scale = 1 / math.sqrt(D)
+    q, k, v = _inputs(S % 991, B, S, S, Hq, Hkv, D, torch.bfloat16)
+    pos = np.arange(S, dtype=np.int64)
+    rows = _rows(S, S + 1)
+    ref_o, ref_l = oracle.attention_rows(q.float().numpy(), k.float().numpy(), v.float().numpy(), pos, pos,
+                                         scale, rows=rows)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    tp = torch.from_numpy(pos).to(DEV)
+    for name, kvp in (("shared positions", tp), ("separate positions", tp.clone())):
+        out, lse = cp.block_fwd(qd, kd, vd, tp, kvp, scale)
+        torch.cuda.synchronize()
+        _check_rows(out, lse, rows, ref_o, ref_l, name)
+
+
+def test_bf16_head_dim_64_ring_share():
+    """A zigzag rank's whole share in one launch at D = 64, sampled rows against the oracle."""
+    C, t, Hq, Hkv, D = 4, 1500, 16, 4, 64
+    S, r = 2 * C * t, 2
+    scale = 1 / math.sqrt(D)
+    q_full, k_full, v_full = _inputs(78, 1, S, S, Hq, Hkv, D, torch.bfloat16)
+    pos = [oracle.zigzag_positions(S, C, o) for o in range(C)]
+    tpos = [torch.from_numpy(p).to(DEV) for p in pos]
+    q = q_full[:, pos[r]].contiguous().to(DEV)
+    ks = [k_full[:, p].contiguous().to(DEV) for p in pos]
+    vs = [v_full[:, p].contiguous().to(DEV) for p in pos]
+    rows = _rows(2 * t, 6)
+    gpos = np.arange(S, dtype=np.int64)
+    ref_o, ref_l = oracle.attention_rows(q_full.float().numpy(), k_full.float().numpy(), v_full.float().numpy(),
+                                         gpos, gpos, scale, rows=pos[r][rows])
+    for mode in ("single", "fused"):
+        out, lse = cp.ring_share_fwd(q, ks, vs, tpos, r, scale, mode=mode)
+        torch.cuda.synchronize()
+        _check_rows(out, lse, rows, ref_o, ref_l, f"D=64 share ({mode})")

@@ -32,11 +32,14 @@ def _full_kv_f32(w, heads):
     return gen(w, "k", ids, heads).float().numpy(), gen(w, "v", ids, heads).float().numpy()
 
 
-def _ring_share(w, r, ks, vs):
+def _ring_share(w, r, ks, vs, mode="single"):
+    """Rank r's share: one launch over the C blocks ("single"), or the ring's per-step form,
+    one launch per step merging in its epilogue ("fused") or into a tile followed by the
+    merge kernel ("unfused")."""
     C = w.cp_size
     pos = [cp.zigzag_index(w.seq_len, C, o, device=DEV) for o in range(C)]
     q = gen(w, "q", zigzag_chunks(C, r), w.heads_q)
-    out, lse = cp.ring_share_fwd(q.to(DEV), ks, vs, pos, r, w.scale)
+    out, lse = cp.ring_share_fwd(q.to(DEV), ks, vs, pos, r, w.scale, mode=mode)
     torch.cuda.synchronize()
     return q, out, lse
 
@@ -66,16 +69,24 @@ def test_tiny_fp32_every_rank_and_step():
 
 
 def test_rank_share_8k_all_rows():
+    """Every row of the 8K rank share against the oracle, in the one-launch form and in the
+    ring's per-step forms (the per-step tile merges of "On Context Parallelism",
+    Peer-to-peer / Forward); the two per-step forms give the same bits."""
     w = WORKLOADS["rank_share_8k"]
     ks, vs = _owner_blocks(w, w.heads_kv)
-    q, out, lse = _ring_share(w, w.rank, ks, vs)
     kf, vf = _full_kv_f32(w, w.heads_kv)
     zz = oracle.zigzag_positions(w.seq_len, w.cp_size, w.rank)
+    q = gen(w, "q", zigzag_chunks(w.cp_size, w.rank), w.heads_q)
     ref_o, ref_l = oracle.attention_rows(q.float().numpy(), kf, vf, zz, np.arange(w.seq_len), w.scale)
     tol_o, tol_l = TOL[w.dtype]
-    eo, el = max_abs(out.cpu().numpy(), ref_o), max_abs(lse.cpu().numpy(), ref_l)
-    print(f"rank_share_8k: max abs err O {eo:.3g}, lse {el:.3g}")
-    assert eo <= tol_o and el <= tol_l
+    res = {}
+    for mode in ("single", "fused", "unfused"):
+        _, out, lse = _ring_share(w, w.rank, ks, vs, mode)
+        eo, el = max_abs(out.cpu().numpy(), ref_o), max_abs(lse.cpu().numpy(), ref_l)
+        print(f"rank_share_8k ({mode}): max abs err O {eo:.3g}, lse {el:.3g}")
+        assert eo <= tol_o and el <= tol_l, mode
+        res[mode] = (out, lse)
+    assert torch.equal(res["fused"][0], res["unfused"][0]) and torch.equal(res["fused"][1], res["unfused"][1])
 
 
 def test_allgather_32k_reorder_then_attend():
@@ -152,18 +163,25 @@ def test_ulysses_gqa_128k_group():
 
 
 def test_ring_share_256k_sampled():
+    """Sampled rows of the long-context ring share against the oracle: the one-launch form
+    and the ring's per-step forms (8 launches, the 7 merges fused into the epilogue or run
+    by the merge kernel)."""
     w = WORKLOADS["ring_share_256k"]
     ks, vs = _owner_blocks(w, w.heads_kv)
-    q, out, lse = _ring_share(w, w.rank, ks, vs)
-    del ks, vs
-    assert torch.isfinite(lse).all() and torch.isfinite(out).all()
     kf, vf = _full_kv_f32(w, w.heads_kv)
     zz = oracle.zigzag_positions(w.seq_len, w.cp_size, w.rank)
+    q = gen(w, "q", zigzag_chunks(w.cp_size, w.rank), w.heads_q)
     rows = sample_rows(w.local_len, w.chunk_len, seed=w.rank, per_chunk_random=12)
     ref_o, ref_l = oracle.attention_rows(q.float().numpy(), kf, vf, zz, np.arange(w.seq_len), w.scale,
                                          rows=rows)
+    del kf, vf
     ridx = torch.from_numpy(rows).to(DEV)
-    eo, el = max_abs(out[:, ridx].cpu().numpy(), ref_o), max_abs(lse[:, :, ridx].cpu().numpy(), ref_l)
-    print(f"ring_share_256k: max abs err O {eo:.3g}, lse {el:.3g} over {len(rows)} rows")
     tol_o, tol_l = TOL[w.dtype]
-    assert eo <= tol_o and el <= tol_l
+    for mode in ("single", "fused", "unfused"):
+        _, out, lse = _ring_share(w, w.rank, ks, vs, mode)
+        assert torch.isfinite(lse).all() and torch.isfinite(out).all()
+        eo, el = max_abs(out[:, ridx].cpu().numpy(), ref_o), max_abs(lse[:, :, ridx].cpu().numpy(), ref_l)
+        print(f"ring_share_256k ({mode}): max abs err O {eo:.3g}, lse {el:.3g} over {len(rows)} rows")
+        assert eo <= tol_o and el <= tol_l, mode
+        del out, lse
+        torch.cuda.empty_cache()

@@ -81,3 +81,26 @@ def test_merge_special_cases_exact():
     tol_o, tol_l = _fp32_bound(o1, l1, o1, l1)
     assert max_abs(do.cpu().numpy(), o1.numpy()) <= tol_o
     assert max_abs(dl.cpu().numpy(), l1.numpy().astype(np.float64) + np.log(2.0)) <= tol_l
+
+
+def test_merge_long_context_tile_sampled():
+    """The merge at the long-context share's tile size (32768 rows x 32 heads x 128, 512 MiB
+    per operand, as each ring step of the per-step form merges), sampled rows against the
+    oracle's fp64 merge: every (row, head) of 512 seeded rows, a fifth of them empty on one
+    side."""
+    B, S, H, D = 1, 32768, 32, 128
+    g = torch.Generator().manual_seed(32768)
+    o1, l1 = _partial(g, B, S, H, D, 0.2)
+    o2, l2 = _partial(g, B, S, H, D, 0.2)
+    rows = np.sort(np.random.default_rng(5).choice(S, 512, replace=False)).astype(np.int64)
+    rows = np.unique(np.concatenate([rows, [0, 1, S - 2, S - 1]]))
+    ref_o, ref_l = oracle.merge(o1[:, rows].numpy(), l1[:, :, rows].numpy(), o2[:, rows].numpy(),
+                                l2[:, :, rows].numpy())
+    do, dl = o1.to(DEV), l1.to(DEV)
+    cp.lse_merge(do, dl, o2.to(DEV), l2.to(DEV))
+    torch.cuda.synchronize()
+    tol_o, tol_l = _fp32_bound(o1[:, rows], l1[:, :, rows], o2[:, rows], l2[:, :, rows])
+    ridx = torch.from_numpy(rows).to(DEV)
+    assert max_abs(do[:, ridx].cpu().numpy(), ref_o) <= tol_o
+    assert max_abs(dl[:, :, ridx].cpu().numpy(), ref_l) <= tol_l
+    assert not torch.isnan(do).any() and not torch.isnan(dl).any()
