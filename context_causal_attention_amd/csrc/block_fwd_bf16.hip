@@ -399,10 +399,14 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
     };
 
     f32x16 acc_o[NB][kD / 32];
-    float m_run[NB], l_run[NB];
+    // m_run: the reference (log2 domain; -inf until the row has a visible key); nm: -m_run as
+    // the fast path adds it, NaN while m_run is unset, so that the fast path's weights and
+    // sum come out NaN and its one bound test also sends an unset row to the exact path
+    float m_run[NB], l_run[NB], nm[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         m_run[nb] = -INFINITY;
+        nm[nb] = __builtin_nanf("");
         l_run[nb] = 0.f;
 #pragma unroll
         for (int db = 0; db < kD / 32; ++db) acc_o[nb][db] = f32x16{};
@@ -486,12 +490,13 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
 
             // softmax in the log2 domain against the running reference m.  Fast path: weights
             // against the current m; they stay bounded (each at most 2^kLazy) whenever this
-            // lane's sum of them does, so no row max is needed.  Otherwise (or while m is unset)
-            // the wave takes the slow path: row max, raise m to it, rescale O and l, recompute.
+            // lane's sum of them does, so no row max is needed.  Otherwise (or while m is unset,
+            // which makes the sum NaN) the wave takes the slow path: row max, raise m to it,
+            // rescale O and l, recompute.  The sums start from their first term (0 + e == e:
+            // every weight is >= +0).
             bf16x8 pb[NB][KBP][2];
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                float m_use = (m_run[nb] == -INFINITY) ? 0.f : m_run[nb];
                 float ts = 0.f;
 #pragma unroll
                 for (int kk = 0; kk < KBP; ++kk)
@@ -499,12 +504,11 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
                     for (int h8 = 0; h8 < 2; ++h8)
 #pragma unroll
                         for (int j = 0; j < 8; ++j) {
-                            const float e = __builtin_amdgcn_exp2f(fmaf(s[nb][kk][8 * h8 + j], p.c, -m_use));
-                            ts += e;
+                            const float e = __builtin_amdgcn_exp2f(fmaf(s[nb][kk][8 * h8 + j], p.c, nm[nb]));
+                            ts = (kk == 0 && h8 == 0 && j == 0) ? e : ts + e;
                             pb[nb][kk][h8][j] = (__bf16)e;
                         }
-                const bool bad = !(ts <= kLazyWeight) || m_run[nb] == -INFINITY;
-                if (__builtin_amdgcn_ballot_w64(bad) != 0) {
+                if (__builtin_amdgcn_ballot_w64(!(ts <= kLazyWeight)) != 0) {
                     float mx = -INFINITY;
 #pragma unroll
                     for (int kk = 0; kk < KBP; ++kk)
@@ -512,13 +516,13 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
                         for (int vv = 0; vv < 16; ++vv) mx = fmaxf(mx, s[nb][kk][vv]);
                     const float mt = half_max(mx) * p.c;
                     const float m_new = fmaxf(m_run[nb], mt);
-                    m_use = (m_new == -INFINITY) ? 0.f : m_new;
+                    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
                     const float alpha = __builtin_amdgcn_exp2f(m_run[nb] - m_use);
                     l_run[nb] *= alpha;
 #pragma unroll
                     for (int db = 0; db < kD / 32; ++db) acc_o[nb][db] *= alpha;
                     m_run[nb] = m_new;
-                    ts = 0.f;
+                    nm[nb] = (m_new == -INFINITY) ? __builtin_nanf("") : -m_new;
 #pragma unroll
                     for (int kk = 0; kk < KBP; ++kk)
 #pragma unroll
@@ -526,7 +530,7 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
 #pragma unroll
                             for (int j = 0; j < 8; ++j) {
                                 const float e = __builtin_amdgcn_exp2f(fmaf(s[nb][kk][8 * h8 + j], p.c, -m_use));
-                                ts += e;
+                                ts = (kk == 0 && h8 == 0 && j == 0) ? e : ts + e;
                                 pb[nb][kk][h8][j] = (__bf16)e;
                             }
                 }

@@ -23,8 +23,9 @@
  *   returned when the HIP runtime reports an error for a launch.
  *   cpattn_last_error() gives a human-readable reason for the last failure on the
  *   calling thread.
- * - Sizes are int64 and all address arithmetic is 64-bit (tensors above 2^31 elements
- *   are supported).
+ * - Sizes are int64 and address arithmetic is 64-bit (tensors above 2^31 elements are
+ *   supported), except a lane's offset within one tile of up to 128 rows, which the bf16
+ *   kernels form in 32 bits: their calls bound a row at 2^24 elements.
  * - The library is stateless; calls on different streams may run concurrently as long
  *   as their buffers do not overlap.
  */
