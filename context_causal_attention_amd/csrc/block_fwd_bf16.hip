@@ -73,6 +73,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.0f;       // raise the running max only past this margin (log2)
 constexpr float kLazyWeight = 256.0f;  // 2^kLazy
 constexpr int kMaxBlocks = kMaxRingBlocks;  // K/V blocks of one launch
+constexpr int kVisKeys = 256;               // key positions a wave searches in LDS
 
 // One K/V block: keys [B][seq][heads_kv][D] and their positions.
 struct KVBlock {
@@ -187,7 +188,6 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
     // (with the keys split over KS wave groups, each group has its own pair of stages)
     __shared__ __attribute__((aligned(16))) char lds_stage0[KS * 2 * kTileBytes];  // [group][K|V][tile]
     __shared__ __attribute__((aligned(16))) char lds_stage1[KS * 2 * kTileBytes];
-    __shared__ int red[2 * NW];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -222,36 +222,41 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
     const int64_t pmax = p.qpos[q_last];
 
     // ---- per K/V block: visible tiles (a prefix) and tiles visible to every query of this
-    // workgroup; then the tile sequence runs over the blocks in turn
+    // workgroup, wave w counting blocks w, w + NW, ... in one pass (four tiles per lane in
+    // flight); then the tile sequence runs over the blocks in turn
     __shared__ int blk_ne[kMaxBlocks], blk_full[kMaxBlocks];
-    for (int o = 0; o < p.n_blk; ++o) {
+    __shared__ int64_t vis_keys[NW][kVisKeys];  // each wave's copy of a block's diagonal positions
+    for (int o = w; o < p.n_blk; o += NW) {
         const int64_t* kp = p.blk[o].pos;
         const int64_t seq_o = p.blk[o].seq;
         const int64_t n_tiles = (seq_o + kBN - 1) / kBN;
         int c_ne = 0, c_full = 0;
-        for (int64_t t = tid; t < n_tiles; t += kThreads) {
-            c_ne += (kp[t * kBN] <= pmax) ? 1 : 0;
-            const int64_t lk = t * kBN + kBN - 1;
-            c_full += (lk < seq_o && kp[lk] <= pmin) ? 1 : 0;
+        for (int64_t t0 = lane; t0 < n_tiles; t0 += 4 * 64) {
+            int64_t first[4], last[4];
+            bool has_f[4], has_l[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int64_t t = t0 + 64 * u;
+                const int64_t lk = t * kBN + kBN - 1;
+                has_f[u] = t < n_tiles;
+                has_l[u] = has_f[u] && lk < seq_o;
+                first[u] = has_f[u] ? kp[t * kBN] : 0;
+                last[u] = has_l[u] ? kp[lk] : 0;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                c_ne += (has_f[u] && first[u] <= pmax) ? 1 : 0;
+                c_full += (has_l[u] && last[u] <= pmin) ? 1 : 0;
+            }
         }
         c_ne = wave_sum(c_ne);
         c_full = wave_sum(c_full);
         if (lane == 0) {
-            red[w] = c_ne;
-            red[NW + w] = c_full;
+            blk_ne[o] = c_ne;
+            blk_full[o] = c_full;
         }
-        __syncthreads();
-        if (tid == 0) {
-            int a = 0, f = 0;
-            for (int i = 0; i < NW; ++i) {
-                a += red[i];
-                f += red[NW + i];
-            }
-            blk_ne[o] = a;
-            blk_full[o] = f;
-        }
-        __syncthreads();
     }
+    __syncthreads();
     int n_total = 0;  // tiles over all blocks
     for (int o = 0; o < p.n_blk; ++o) n_total += blk_ne[o];
 
@@ -353,6 +358,27 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
     };
 
     // ---- this lane's query rows; Q as MFMA B operands (16 dims x 32 queries per step)
+    // ---- the first tile of this (key group's) sequence goes out now, so that its latency
+    // overlaps the reads of the query rows and of the diagonal positions below
+    LDS_AS char* st0 = (LDS_AS char*)lds_stage0 + ksg * 2 * kTileBytes;
+    LDS_AS char* st1 = (LDS_AS char*)lds_stage1 + ksg * 2 * kTileBytes;
+    while (oc < p.n_blk && blk_ne[oc] == 0) ++oc;  // first block with a visible tile
+    ne_c = ne_of(oc);
+    // key group g starts at tile g of the sequence
+    for (int s2 = 0; s2 < ksg; ++s2)
+        if (oc < p.n_blk) adv_c();
+    if (oc < p.n_blk) {
+        set_load(oc, jt);
+        issue_tile(st0);
+        if (KS == 1) {
+            adv_n();
+        } else {
+#pragma unroll
+            for (int s2 = 0; s2 < KS; ++s2)
+                if (on < p.n_blk) adv_n();
+        }
+    }
+
     bf16x8 qreg[NB][kD / 16];
     int64_t myq[NB];
     int64_t myh[NB];
@@ -378,23 +404,45 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
     // number of keys of block o visible to each of this lane's query rows, needed only when
     // some tile of o is partly visible: positions increase, so it is found by binary search
     // within the keys of the partly visible tiles [n_full*kBN, min(n_ne*kBN, seq))
+    // within the keys of the partly visible tiles [n_full*kBN, min(n_ne*kBN, seq)).  At the
+    // start (use_lds), when they are few (at most kVisKeys: a block's diagonal), the wave
+    // copies their positions into its own slice of LDS once and searches there; otherwise,
+    // and for blocks entered later (whose rows are in the zigzag shares all or nothing, so
+    // no search runs), it searches global memory.
     int64_t vis[NB];
-    auto find_vis = [&](int o) {
+    auto find_vis = [&](int o, bool use_lds) {
         const int ne = blk_ne[o], full = blk_full[o];
         const int64_t seq_o = p.blk[o].seq;
         const int64_t* kp = p.blk[o].pos;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            vis[nb] = 0;
-            if (full < ne) {
-                int64_t lo = (int64_t)full * kBN;
-                int64_t hi = (int64_t)ne * kBN < seq_o ? (int64_t)ne * kBN : seq_o;
+        for (int nb = 0; nb < NB; ++nb) vis[nb] = 0;
+        if (full >= ne) return;
+        const int64_t lo0 = (int64_t)full * kBN;
+        const int64_t hi0 = (int64_t)ne * kBN < seq_o ? (int64_t)ne * kBN : seq_o;
+        const int n = (int)(hi0 - lo0 < kVisKeys + 1 ? hi0 - lo0 : kVisKeys + 1);
+        if (use_lds && n <= kVisKeys) {
+            LDS_AS int64_t* vk = (LDS_AS int64_t*)&vis_keys[w][0];
+            for (int i = lane; i < n; i += 64) vk[i] = kp[lo0 + i];
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's copies are in LDS
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                int lo = 0, hi = n;
                 while (lo < hi) {
-                    const int64_t mid = (lo + hi) >> 1;
-                    if (kp[mid] <= mypos[nb]) lo = mid + 1; else hi = mid;
+                    const int mid = (lo + hi) >> 1;
+                    if (vk[mid] <= mypos[nb]) lo = mid + 1; else hi = mid;
                 }
-                vis[nb] = lo;
+                vis[nb] = lo0 + lo;
             }
+            return;
+        }
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            int64_t lo = lo0, hi = hi0;
+            while (lo < hi) {
+                const int64_t mid = (lo + hi) >> 1;
+                if (kp[mid] <= mypos[nb]) lo = mid + 1; else hi = mid;
+            }
+            vis[nb] = lo;
         }
     };
 
@@ -430,8 +478,6 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
         off_v[db] = vkey * kRowBytes + ((chunk ^ vsw) << 4) + ((s16 & 1) << 3);
     }
 
-    LDS_AS char* st0 = (LDS_AS char*)lds_stage0 + ksg * 2 * kTileBytes;
-    LDS_AS char* st1 = (LDS_AS char*)lds_stage1 + ksg * 2 * kTileBytes;
 
     // one tile: prefetch the next tile into `nxt`, compute the current one from `cur`
     auto tile = [&](const LDS_AS char* kt, LDS_AS char* nxt) {
@@ -578,27 +624,13 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
         }
         if (oc != o_prev && oc < p.n_blk) {
             n_full = __builtin_amdgcn_readfirstlane(blk_full[oc]);
-            find_vis(oc);
+            find_vis(oc, false);
         }
     };
 
-    while (oc < p.n_blk && blk_ne[oc] == 0) ++oc;  // first block with a visible tile
-    ne_c = ne_of(oc);
-    // key group g starts at tile g of the sequence
-    for (int s2 = 0; s2 < ksg; ++s2)
-        if (oc < p.n_blk) adv_c();
     if (oc < p.n_blk) {
         n_full = __builtin_amdgcn_readfirstlane(blk_full[oc]);
-        find_vis(oc);
-        set_load(oc, jt);
-        issue_tile(st0);
-        if (KS == 1) {
-            adv_n();
-        } else {
-#pragma unroll
-            for (int s2 = 0; s2 < KS; ++s2)
-                if (on < p.n_blk) adv_n();
-        }
+        find_vis(oc, true);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), visible to the compiler
     __syncthreads();
