@@ -614,6 +614,31 @@ def hbm_flushed(plan, reps: int = 5, flush_mib: int = 1024):
                     "GB/s": round(nbytes / (med * 1e-3) / 1e9, 1),
                     "frac_of_hbm_peak": round(nbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                     "flush": f"{flush_mib} MiB scratch write before each of {reps} repetitions"})
+    # the runtime's own device copy of the largest and the smallest call's bytes under the same
+    # flush: what a plain copy of that size reaches on this chip, beside the kernels
+    sizes = sorted({c[1] for c in calls})
+    src = torch.empty(sizes[-1] // 2, dtype=torch.uint8, device=plan.dev)
+    dst = torch.empty_like(src)
+    for nbytes in sorted({sizes[0], sizes[-1]}):
+        sv, dv = src[: nbytes // 2], dst[: nbytes // 2]
+        dv.copy_(sv)  # warm
+        ms = []
+        for i in range(reps):
+            scratch.fill_(float(i))
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            dv.copy_(sv)
+            e.record()
+            torch.cuda.synchronize()
+            ms.append(s.elapsed_time(e))
+        ms.sort()
+        med = ms[len(ms) // 2]
+        out.append({"kernel": "device copy, reference (torch copy_)", "bytes_per_call": nbytes,
+                    "median_ms": round(med, 4), "min_ms": round(ms[0], 4),
+                    "GB/s": round(nbytes / (med * 1e-3) / 1e9, 1),
+                    "frac_of_hbm_peak": round(nbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                    "flush": f"{flush_mib} MiB scratch write before each of {reps} repetitions"})
+    del src, dst
     del scratch
     return out
 
