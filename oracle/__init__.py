@@ -73,10 +73,11 @@ def _load():
     L.orc_merge.argtypes = [P, P, P, P, i32, i64, i32, i32]
     L.orc_combine_blocks.argtypes = [P, P, P, i32, i64, i32, P, P]
     L.orc_block_bwd.argtypes = [P, P, P, P, P, P, i32, i64, i64, i32, i32, i32, P, P, f64, P, i64, P,
-                                i64, P, P, P, i32]
+                                i64, P, P, P, i32, i32]
+    L.orc_round_bf16.argtypes = [P, P, i64]
     for name in ("orc_zigzag_positions", "orc_contiguous_positions", "orc_gathered_positions",
                  "orc_reorder", "orc_ulysses_permute", "orc_attention_rows", "orc_block_stats",
-                 "orc_merge", "orc_combine_blocks", "orc_block_bwd"):
+                 "orc_merge", "orc_combine_blocks", "orc_block_bwd", "orc_round_bf16"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -238,11 +239,23 @@ def combine_blocks(m, l, z):
     return out, lse
 
 
+def round_bf16(x) -> np.ndarray:
+    """Each value rounded to the nearest bf16 value, ties to even (``orc_round_bf16``)."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    y = np.empty_like(x)
+    _check(_load().orc_round_bf16(_ptr(x), _ptr(y), x.size), "round_bf16")
+    return y
+
+
 def block_bwd(q, k, v, dout, out, lse, q_pos, kv_pos, scale: float, qrows=None, krows=None,
-              nthreads: int | None = None):
+              nthreads: int | None = None, bf16_pds: bool = False):
     """Backward of one block (see ``orc_block_bwd``): returns (dq, dk, dv) in fp64 for the
     selected query rows (default all) and key rows (default all).  out and lse are the
-    complete forward results of the query rows (fp64 or fp32 values)."""
+    complete forward results of the query rows (fp64 or fp32 values).
+
+    bf16_pds: a model of a bf16 backward that rounds the two operands it forms itself to
+    bf16 before the products that use them: p (for dv) and ds = p (dp - D) (for dq and dk,
+    formed from the unrounded p); everything else stays fp64."""
     q, k, v, dout = _f32(q), _f32(k), _f32(v), _f32(dout)
     out = np.ascontiguousarray(out, dtype=np.float64)
     lse = np.ascontiguousarray(lse, dtype=np.float64)
@@ -257,7 +270,7 @@ def block_bwd(q, k, v, dout, out, lse, q_pos, kv_pos, scale: float, qrows=None, 
     dv = np.empty((B, len(kr), Hkv, D))
     _check(_load().orc_block_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(out), _ptr(lse), B, Sq, Skv,
                                  Hq, Hkv, D, _ptr(qp), _ptr(kp), float(scale), _ptr(qr), len(qr), _ptr(kr),
-                                 len(kr), _ptr(dq), _ptr(dk), _ptr(dv),
+                                 len(kr), _ptr(dq), _ptr(dk), _ptr(dv), 1 if bf16_pds else 0,
                                  nthreads or default_threads()), "block_bwd")
     return dq, dk, dv
 

@@ -343,6 +343,7 @@ typedef struct {
     int64_t nq, nk;
     double scale;
     double *dq, *dk, *dv;
+    int32_t bf16_pds;
     int64_t next;
     pthread_mutex_t mu;
 } bwd_job_t;
@@ -355,7 +356,27 @@ static double bwd_delta(const bwd_job_t* J, int64_t b, int64_t h, int64_t i) {
     return s;
 }
 
-/* p_ij and ds_ij of one visible pair (query row i of head h, key row j of kv head c) */
+/* x rounded to the nearest bf16 value, ties to even (bf16: 8 significant bits, the fp32
+ * exponent range, subnormals below 2^-126 in steps of 2^-133).  Exact for finite x of
+ * magnitude below the largest bf16; nearbyint rounds ties to even in the default mode. */
+static double round_bf16(double x) {
+    if (x == 0.0 || !isfinite(x)) return x;
+    if (fabs(x) < ldexp(1.0, -126)) return nearbyint(ldexp(x, 133)) * ldexp(1.0, -133);
+    int e;
+    const double m = frexp(x, &e); /* x = m 2^e, 0.5 <= |m| < 1 */
+    return ldexp(nearbyint(ldexp(m, 8)), e - 8);
+}
+
+int orc_round_bf16(const double* x, double* y, int64_t n) {
+    if (n < 0) return ORC_BAD;
+    for (int64_t i = 0; i < n; ++i) y[i] = round_bf16(x[i]);
+    return ORC_OK;
+}
+
+/* p_ij and ds_ij of one visible pair (query row i of head h, key row j of kv head c).
+ * With bf16_pds set (a model of a bf16 backward that rounds the two matrix-product
+ * operands it forms itself), p is rounded to bf16 for its use in dv, and ds is rounded
+ * after being formed from the unrounded p; all else stays fp64. */
 static void bwd_pair(const bwd_job_t* J, int64_t b, int64_t h, int64_t i, int64_t c, int64_t j,
                      double delta, double* p, double* ds) {
     const int64_t D = J->D;
@@ -370,6 +391,10 @@ static void bwd_pair(const bwd_job_t* J, int64_t b, int64_t h, int64_t i, int64_
     }
     *p = exp(s * J->scale - J->lse[(b * J->Hq + h) * J->Sq + i]);
     *ds = *p * (dp - delta);
+    if (J->bf16_pds) {
+        *p = round_bf16(*p);
+        *ds = round_bf16(*ds);
+    }
 }
 
 static void* bwd_worker(void* arg) {
@@ -426,13 +451,13 @@ int orc_block_bwd(const float* q, const float* k, const float* v, const float* d
                   const double* lse, int32_t B, int64_t Sq, int64_t Skv, int32_t Hq, int32_t Hkv, int32_t D,
                   const int64_t* qpos, const int64_t* kvpos, double scale, const int64_t* qrows,
                   int64_t nq, const int64_t* krows, int64_t nk, double* dq, double* dk, double* dv,
-                  int32_t nthreads) {
+                  int32_t bf16_pds, int32_t nthreads) {
     if (B <= 0 || Sq < 0 || Skv < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv != 0) return ORC_BAD;
     if (nq < 0 || nk < 0) return ORC_BAD;
     for (int64_t r = 0; r < nq; ++r) if (qrows[r] < 0 || qrows[r] >= Sq) return ORC_BAD;
     for (int64_t r = 0; r < nk; ++r) if (krows[r] < 0 || krows[r] >= Skv) return ORC_BAD;
     bwd_job_t J = {q, k, v, dout, out, lse, B, Sq, Skv, Hq, Hkv, D, qpos, kvpos, qrows, krows,
-                   nq, nk, scale, dq, dk, dv, 0};
+                   nq, nk, scale, dq, dk, dv, bf16_pds ? 1 : 0, 0};
     pthread_mutex_init(&J.mu, NULL);
     if (nthreads < 1) nthreads = 1;
     pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);

@@ -122,3 +122,49 @@ def test_backward_contribution_pattern_rank1():
     g = read_golden("backward_contrib_rank1_c4.txt")
     for key, qchunks in g.items():
         assert reach[int(key.split()[1])] == [int(c) for c in qchunks]
+
+
+# ---- the bf16 rounding model (p and ds rounded to bf16 before the products that use them)
+def test_round_bf16_matches_torch_conversion():
+    """The rounding primitive against torch's float32 -> bfloat16 conversion (round to nearest,
+    ties to even) on fp32 values: random magnitudes over the whole exponent range, exact ties
+    (low 16 bits 0x8000, both parities of the kept bit), and subnormals."""
+    rng = np.random.default_rng(11)
+    bits = rng.integers(0, 2 ** 32, 20000, dtype=np.uint64).astype(np.uint32)
+    x = bits.view(np.float32)
+    x = x[np.isfinite(x) & (np.abs(x) < 3.0e38)]
+    ties = ((bits & np.uint32(0xFFFF0000)) | np.uint32(0x8000)).view(np.float32)
+    ties = ties[np.isfinite(ties) & (np.abs(ties) < 3.0e38)]
+    sub = (rng.integers(1, 2 ** 23, 2000, dtype=np.uint64).astype(np.uint32)).view(np.float32)
+    for vals in (x, ties, sub, -sub, np.float32([0.0, -0.0, 1.0, 1.00390625, 1.01171875])):
+        want = torch.from_numpy(vals).to(torch.bfloat16).to(torch.float64).numpy()
+        got = oracle.round_bf16(vals.astype(np.float64))
+        np.testing.assert_array_equal(got, want)
+
+
+def test_bwd_bf16_model_within_rounding_bound():
+    """Each term of a gradient sum carries one bf16 rounding (of p in dv, of ds in dq and dk),
+    at most 2^-9 of itself; on these N(0,1) inputs the model stays within 2^-6 of the largest
+    entry of the exact backward, and the rounding does take effect (the results differ)."""
+    B, S, Hq, Hkv, D, scale = 1, 40, 4, 2, 16, 0.25
+    q, k, v, dout = _inputs(21, B, S, Hq, Hkv, D)
+    pos = np.arange(S, dtype=np.int64)
+    out, lse = oracle.attention_rows(q, k, v, pos, pos, scale)
+    exact = oracle.block_bwd(q, k, v, dout, out, lse, pos, pos, scale)
+    model = oracle.block_bwd(q, k, v, dout, out, lse, pos, pos, scale, bf16_pds=True)
+    for e, m in zip(exact, model):
+        diff = float(np.max(np.abs(e - m)))
+        assert 0.0 < diff <= 2.0 ** -6 * float(np.max(np.abs(e)))
+
+
+def test_bwd_bf16_model_exact_when_p_is_one():
+    """One query that sees one key: p = 1 and ds = 0 are bf16 values, so the model equals the
+    exact backward (dq = dk = 0, dv = dout)."""
+    q, k, v, dout = _inputs(22, 1, 1, 2, 1, 8)
+    pos = np.zeros(1, dtype=np.int64)
+    out, lse = oracle.attention_rows(q, k, v, pos, pos, 0.5)
+    exact = oracle.block_bwd(q, k, v, dout, out, lse, pos, pos, 0.5)
+    model = oracle.block_bwd(q, k, v, dout, out, lse, pos, pos, 0.5, bf16_pds=True)
+    for e, m in zip(exact, model):
+        np.testing.assert_array_equal(e, m)
+    np.testing.assert_array_equal(model[2][0, 0, 0], dout[0, 0].astype(np.float64).sum(axis=0))
