@@ -23,6 +23,11 @@ the pages step by step:
 * the work models of "Context Parallelism & Ring Attention" ("The causal load-imbalance
   problem", "The zigzag fix") and of "Context parallelism: Ring Attention and Ulysses"
   ("The zigzag partition", "Ring Attention").
+
+``block_bwd(..., bf16_pds=True)`` (with ``round_bf16``, its rounding) is not a step of the
+pages, which fix no precision: it models a bf16 backward that rounds its two self-formed
+product operands, p and ds, to bf16, so that such a kernel's rounding can be checked
+exactly rather than only bounded.
 """
 from __future__ import annotations
 
