@@ -71,8 +71,8 @@ def parse_args(argv=None):
                          "small workloads); the attention launches are then timed as part of the step")
     ap.add_argument("--extras", default=None,
                     help="comma-separated workload[:mode] list measured after the main line and reported "
-                         "under 'extra' (default: the Ulysses group and the per-step ring share when the "
-                         "main line is the default one; '' for none)")
+                         "under 'extra' (default: the Ulysses group in its explicit and its fused form and "
+                         "the per-step ring share when the main line is the default one; '' for none)")
     ap.add_argument("--no-flush", action="store_true",
                     help="skip the bandwidth-bound kernels' separate timing under the MALL flush")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -762,11 +762,12 @@ def main(argv=None) -> int:
 
 
 # Measured beside the default line, in the same run: the Ulysses group with the workload's
-# explicit permute, attention and inverse permute ("On Context Parallelism", All-to-all),
-# and the long-context ring share in its per-step form, one attention launch per ring step
-# into a tile and the merge kernel after each ("On Context Parallelism", Peer-to-peer /
-# Forward).
-EXTRAS = [("ulysses_gqa_128k", "single"), ("ring_share_256k", "unfused")]
+# explicit permute, attention and inverse permute ("On Context Parallelism", All-to-all); the
+# same group as the library's Ulysses share runs it, the exchanges folded into the attention's
+# row addressing; and the long-context ring share in its per-step form, one attention launch
+# per ring step into a tile and the merge kernel after each ("On Context Parallelism",
+# Peer-to-peer / Forward).
+EXTRAS = [("ulysses_gqa_128k", "single"), ("ulysses_gqa_128k", "fused"), ("ring_share_256k", "unfused")]
 
 
 if __name__ == "__main__":
