@@ -584,7 +584,12 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
             }
 
             // O^T += V^T P^T (the four accumulators interleaved: a product never waits on the
-            // one just issued)
+            // one just issued).  The wave issues these at raised priority: when several waves of
+            // a SIMD are ready, the arbiter takes the one with output products to issue, so the
+            // matrix pipe stays fed while the others' softmax fills the gaps (+1.6% on the ring
+            // share and the Ulysses group at the same or a lower clock; the same raise around
+            // the score products, or around both, gained less or lost)
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int kk = 0; kk < KBP; ++kk) {
 #pragma unroll
@@ -607,6 +612,7 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
             }
             __builtin_amdgcn_sched_group_barrier(0x008, NB * kReadAheadV, 2);
+            __builtin_amdgcn_s_setprio(0);
         }
         // the next tile has landed in LDS (own loads) and every wave is done with this one
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), visible to the compiler
