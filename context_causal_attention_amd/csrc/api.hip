@@ -279,8 +279,6 @@ CPATTN_API cpattn_status_t cpattn_block_bwd(const void* q, const void* k, const 
         return fail(CPATTN_ERR_SHAPE, "%s: heads_q %d not a multiple of heads_kv %d", name, heads_q, heads_kv);
     if (head_dim != 64 && head_dim != 128)
         return fail(CPATTN_ERR_UNSUPPORTED, "%s: head_dim %d (supported: 64, 128)", name, head_dim);
-    if (dtype == CPATTN_BF16 && head_dim != 128)
-        return fail(CPATTN_ERR_UNSUPPORTED, "%s: bf16 path supports head_dim 128 only", name);
     if (dtype == CPATTN_BF16 && (int64_t)heads_q * head_dim > kMaxRowElems)
         return fail(CPATTN_ERR_UNSUPPORTED, "%s: heads_q * head_dim = %lld above 2^24", name,
                     (long long)heads_q * head_dim);

@@ -48,14 +48,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_AS __attribute__((address_space(3)))
 
-constexpr int kD = 128;
-constexpr int kRowBytes = kD * 2;
 constexpr int kTile = 64;                   // keys (dq kernel) or queries (dk/dv kernel) per tile
-constexpr int kTileBytes = kTile * kRowBytes;
 constexpr int kNW = 4;                      // waves per block
 constexpr int kThreads = 64 * kNW;
-constexpr int kRowsPerWave = kTile / kNW;   // tile rows each wave loads
-constexpr int kLoads = kRowsPerWave / 4;    // 16-byte loads per lane per tensor and tile
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct BwdParams {
@@ -141,34 +136,49 @@ __device__ inline void sched_reads_ahead() {
     __builtin_amdgcn_sched_group_barrier(0x008, M * A, G);
 }
 
-// Tiles in LDS are row-major (256 bytes per row) with 16-byte chunk c of row r stored at
-// chunk c ^ swz(r), swz(r) = ((r & 3) << 2) | ((r >> 2) & 3).  Over 16 aligned rows swz is a
-// permutation of 0..15, so a row read of 16 consecutive rows at one chunk touches 16 distinct
-// chunk slots; over 4 aligned rows its top two bits differ, so a transposed read of 4 rows x 4
-// chunks (one 32-lane pass) also touches 16 distinct slots.  Both are free of bank conflicts.
-__device__ inline int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
-//
-// Row-read offsets (matrix-core A operand, 32 rows x 16 columns, lane = row l32 holding
-// columns 16*ks + 8*half .. +7): row l32 of a 32-row block.
-__device__ inline uint32_t row_off(int lane, int ks) {
-    const int l32 = lane & 31, half = lane >> 5;
-    return l32 * kRowBytes + (((2 * ks + half) ^ swz(l32)) << 4);
-}
-// Transposed-read offsets (A operand = columns 32*db .. +31 as rows, 16 tile rows as k): the
-// k order is the accumulator's row order 16*ks2 + 8*(j/4) + 4*half + j%4, so that an operand
-// packed straight from an accumulator lines up.  Two 8-byte reads per operand: tile rows
-// vkey and vkey + 8 of the 16-row step.
+// Tiles in LDS are row-major (D bf16 per row) with 16-byte chunk c of row r stored at chunk
+// c ^ swz(r).
+//   D = 128 (256-byte rows, one per bank row): swz(r) = ((r & 3) << 2) | ((r >> 2) & 3).  Over
+//   16 aligned rows swz is a permutation of 0..15, so a row read of 16 consecutive rows at one
+//   chunk touches 16 distinct chunk slots; over 4 aligned rows its top two bits differ, so a
+//   transposed read of 4 rows x 4 chunks (one 32-lane pass) also touches 16 distinct slots.
+//   D = 64 (128-byte rows, two per bank row: even rows in its first half, odd rows in its
+//   second): swz(r) = (((r >> 1) & 1) << 2) | ((r >> 2) & 3).  Over 16 aligned rows it is a
+//   permutation of 0..7 on the even rows and on the odd rows, so a row read again touches 16
+//   distinct slots; in 4 aligned rows the two even (and the two odd) rows differ in its top
+//   bit, so a transposed read's 4 aligned chunks land in the two halves of the bank row.
+// Both access patterns are free of bank conflicts at either width.
 struct TrOff {
     uint32_t a, b;
 };
-__device__ inline TrOff tr_off(int lane, int db) {
-    const int half = lane >> 5, grp = lane >> 4, s16 = lane & 15;
-    const int vkey = 4 * half + (s16 >> 2);
-    const int chunk = 4 * db + 2 * (grp & 1) + ((s16 & 3) >> 1);
-    const uint32_t lo = (s16 & 1) << 3;
-    return TrOff{vkey * kRowBytes + ((chunk ^ swz(vkey)) << 4) + lo,
-                 (vkey + 8) * kRowBytes + ((chunk ^ swz(vkey + 8)) << 4) + lo};
-}
+template <int D> struct BwdGeom {
+    static_assert(D == 64 || D == 128, "head dim 64 or 128");
+    static constexpr int kRowBytes = D * 2;
+    static constexpr int kTileBytes = kTile * kRowBytes;
+    static constexpr int kChunks = D / 8;              // 16-byte chunks per row
+    static constexpr int kRowsPerLoad = 64 / kChunks;  // rows one 64-lane 16-byte load fills
+    __device__ static inline int swz(int r) {
+        return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+    }
+    // Row-read offsets (matrix-core A operand, 32 rows x 16 columns, lane = row l32 holding
+    // columns 16*ks + 8*half .. +7): row l32 of a 32-row block.
+    __device__ static inline uint32_t row_off(int lane, int ks) {
+        const int l32 = lane & 31, half = lane >> 5;
+        return l32 * kRowBytes + (((2 * ks + half) ^ swz(l32)) << 4);
+    }
+    // Transposed-read offsets (A operand = columns 32*db .. +31 as rows, 16 tile rows as k):
+    // the k order is the accumulator's row order 16*ks2 + 8*(j/4) + 4*half + j%4, so that an
+    // operand packed straight from an accumulator lines up.  Two 8-byte reads per operand:
+    // tile rows vkey and vkey + 8 of the 16-row step.
+    __device__ static inline TrOff tr_off(int lane, int db) {
+        const int half = lane >> 5, grp = lane >> 4, s16 = lane & 15;
+        const int vkey = 4 * half + (s16 >> 2);
+        const int chunk = 4 * db + 2 * (grp & 1) + ((s16 & 3) >> 1);
+        const uint32_t lo = (s16 & 1) << 3;
+        return TrOff{vkey * kRowBytes + ((chunk ^ swz(vkey)) << 4) + lo,
+                     (vkey + 8) * kRowBytes + ((chunk ^ swz(vkey + 8)) << 4) + lo};
+    }
+};
 
 // ------------------------------------------------------------------------------------------
 // dq kernel
@@ -176,12 +186,18 @@ __device__ inline TrOff tr_off(int lane, int db) {
 // KS = 1: 4 waves, each over both 32-key halves of every K/V tile.  KS = 2 (launches too small
 // to fill the chip): 8 waves, two per 32-row query group, one per 32-key half of every tile,
 // each with its own partial dQ; the second-half waves hand theirs over through LDS at the end.
-template <int KS>
+template <int D, int KS>
 __global__ void __launch_bounds__(64 * kNW * KS, 1) block_bwd_dq_kernel(const BwdParams p) {
+    using BG = BwdGeom<D>;
+    constexpr int kD = D;
+    constexpr int kRowBytes = BG::kRowBytes;
+    constexpr int kTileBytes = BG::kTileBytes;
+    constexpr int kRPL = BG::kRowsPerLoad;
     constexpr int NW = kNW * KS;
     constexpr int kThr = 64 * NW;
     constexpr int kRowsW = kTile / NW;  // tile rows each wave loads
-    constexpr int kLd = kRowsW / 4;
+    static_assert(kRowsW % kRPL == 0, "whole loads per wave");
+    constexpr int kLd = kRowsW / kRPL;
     constexpr int NKB = 2 / KS;         // 32-key halves of a tile each wave takes
     __shared__ __attribute__((aligned(16))) char lds_stage0[2 * kTileBytes];  // [K|V]
     __shared__ __attribute__((aligned(16))) char lds_stage1[2 * kTileBytes];
@@ -243,13 +259,13 @@ __global__ void __launch_bounds__(64 * kNW * KS, 1) block_bwd_dq_kernel(const Bw
     const char* kbase = (const char*)(p.k + (b * p.seq_kv * p.heads_kv + kvh) * (int64_t)kD);
     const char* vbase = (const char*)(p.v + (b * p.seq_kv * p.heads_kv + kvh) * (int64_t)kD);
     const int64_t tile_bytes_g = (int64_t)kTile * kvstride * 2;
-    const int ld_row_in = lane >> 4;
-    const int ld_chunk = lane & 15;
+    const int ld_row_in = lane / BG::kChunks;
+    const int ld_chunk = lane % BG::kChunks;
     uint32_t koff[kLd];
 #pragma unroll
     for (int i = 0; i < kLd; ++i) {
-        const int row = w * kRowsW + 4 * i + ld_row_in;
-        koff[i] = (uint32_t)(row * kvstride * 2) + ((ld_chunk ^ swz(row)) << 4);
+        const int row = w * kRowsW + kRPL * i + ld_row_in;
+        koff[i] = (uint32_t)(row * kvstride * 2) + ((ld_chunk ^ BG::swz(row)) << 4);
     }
     auto issue_tile = [&](int jt, LDS_AS char* kt) {
         LDS_AS char* vt = kt + kTileBytes;
@@ -262,11 +278,11 @@ __global__ void __launch_bounds__(64 * kNW * KS, 1) block_bwd_dq_kernel(const Bw
         const __amdgpu_buffer_rsrc_t vr = make_rsrc(vb_t, span);
 #pragma unroll
         for (int i = 0; i < kLd; ++i) {
-            const int row = w * kRowsW + 4 * i + ld_row_in;
+            const int row = w * kRowsW + kRPL * i + ld_row_in;
             // rows past the end re-read the last key (finite data the mask hides)
             const uint32_t back = (row > rmax) ? (uint32_t)((row - rmax) * kvstride * 2) : 0u;
-            load_lds16(kr, koff[i] - back, kt + (w * kRowsW + 4 * i) * kRowBytes);
-            load_lds16(vr, koff[i] - back, vt + (w * kRowsW + 4 * i) * kRowBytes);
+            load_lds16(kr, koff[i] - back, kt + (w * kRowsW + kRPL * i) * kRowBytes);
+            load_lds16(vr, koff[i] - back, vt + (w * kRowsW + kRPL * i) * kRowBytes);
         }
     };
 
@@ -307,10 +323,10 @@ __global__ void __launch_bounds__(64 * kNW * KS, 1) block_bwd_dq_kernel(const Bw
 
     uint32_t off_r[kD / 16];
 #pragma unroll
-    for (int ks = 0; ks < kD / 16; ++ks) off_r[ks] = row_off(lane, ks);
+    for (int ks = 0; ks < kD / 16; ++ks) off_r[ks] = BG::row_off(lane, ks);
     TrOff off_t[kD / 32];
 #pragma unroll
-    for (int db = 0; db < kD / 32; ++db) off_t[db] = tr_off(lane, db);
+    for (int db = 0; db < kD / 32; ++db) off_t[db] = BG::tr_off(lane, db);
 
     LDS_AS char* st0 = (LDS_AS char*)lds_stage0;
     LDS_AS char* st1 = (LDS_AS char*)lds_stage1;
@@ -382,8 +398,8 @@ __global__ void __launch_bounds__(64 * kNW * KS, 1) block_bwd_dq_kernel(const Bw
 
     if constexpr (KS > 1) {
         // the key halves' partial sums meet in the first-half waves (each stage holds two
-        // waves' 16 KB; the stages are free after the loop)
-        LDS_AS float* xch = (LDS_AS float*)((qg >> 1) ? lds_stage1 : lds_stage0) + (qg & 1) * (64 * 64);
+        // waves' partials, D/2 KB each; the stages are free after the loop)
+        LDS_AS float* xch = (LDS_AS float*)((qg >> 1) ? lds_stage1 : lds_stage0) + (qg & 1) * ((kD / 32) * 16 * 64);
         if (khalf == 1) {
 #pragma unroll
             for (int db = 0; db < kD / 32; ++db)
@@ -417,13 +433,20 @@ __global__ void __launch_bounds__(64 * kNW * KS, 1) block_bwd_dq_kernel(const Bw
 // ------------------------------------------------------------------------------------------
 // dk/dv kernel
 // ------------------------------------------------------------------------------------------
-constexpr int kStageBytes = 2 * kTileBytes + 2 * kTile * 4;  // [Q | dO | lse2 | D]
 constexpr int kNWkv = 8;                       // dk/dv waves: 4 key groups x 2 query halves
 constexpr int kThreadsKv = 64 * kNWkv;
 constexpr int kRowsPerWaveKv = kTile / kNWkv;  // tile rows each wave loads
-constexpr int kLoadsKv = kRowsPerWaveKv / 4;
 
+template <int D>
 __global__ void __launch_bounds__(kThreadsKv, 1) block_bwd_dkdv_kernel(const BwdParams p) {
+    using BG = BwdGeom<D>;
+    constexpr int kD = D;
+    constexpr int kRowBytes = BG::kRowBytes;
+    constexpr int kTileBytes = BG::kTileBytes;
+    constexpr int kRPL = BG::kRowsPerLoad;
+    constexpr int kStageBytes = 2 * kTileBytes + 2 * kTile * 4;  // [Q | dO | lse2 | D]
+    static_assert(kRowsPerWaveKv % kRPL == 0, "whole loads per wave");
+    constexpr int kLoadsKv = kRowsPerWaveKv / kRPL;
     __shared__ __attribute__((aligned(16))) char lds_stage0[kStageBytes];
     __shared__ __attribute__((aligned(16))) char lds_stage1[kStageBytes];
     __shared__ int red[2 * kNWkv];
@@ -496,7 +519,7 @@ __global__ void __launch_bounds__(kThreadsKv, 1) block_bwd_dkdv_kernel(const Bwd
     if (qhalf == 0) {
 #pragma unroll
         for (int ks = 0; ks < kD / 16; ++ks)
-            *(LDS_AS bf16x8*)(vl + row_off(lane, ks)) = load_row16(p.v + krow * kD + 16 * ks + 8 * half, kvalid);
+            *(LDS_AS bf16x8*)(vl + BG::row_off(lane, ks)) = load_row16(p.v + krow * kD + 16 * ks + 8 * half, kvalid);
     }
     // first query row that sees this key (rows before it are masked), when some tile is partial
     int64_t first = 0;
@@ -514,13 +537,13 @@ __global__ void __launch_bounds__(kThreadsKv, 1) block_bwd_dkdv_kernel(const Bwd
     // Q/dO tile loads: step u is query head h0 + u / nq_vis, query tile qt_lo + u % nq_vis
     const int64_t qstride = (int64_t)p.heads_q * kD;
     const int64_t qtile_bytes_g = (int64_t)kTile * qstride * 2;
-    const int ld_row_in = lane >> 4;
-    const int ld_chunk = lane & 15;
+    const int ld_row_in = lane / BG::kChunks;
+    const int ld_chunk = lane % BG::kChunks;
     uint32_t qoff[kLoadsKv];
 #pragma unroll
     for (int ii = 0; ii < kLoadsKv; ++ii) {
-        const int row = w * kRowsPerWaveKv + 4 * ii + ld_row_in;
-        qoff[ii] = (uint32_t)(row * qstride * 2) + ((ld_chunk ^ swz(row)) << 4);
+        const int row = w * kRowsPerWaveKv + kRPL * ii + ld_row_in;
+        qoff[ii] = (uint32_t)(row * qstride * 2) + ((ld_chunk ^ BG::swz(row)) << 4);
     }
     auto step_of = [&](int u, int64_t& h, int64_t& qt) {
         h = h0 + u / nq_vis;
@@ -537,11 +560,11 @@ __global__ void __launch_bounds__(kThreadsKv, 1) block_bwd_dkdv_kernel(const Bwd
         const __amdgpu_buffer_rsrc_t gr = make_rsrc(gb_t, span);
 #pragma unroll
         for (int ii = 0; ii < kLoadsKv; ++ii) {
-            const int row = w * kRowsPerWaveKv + 4 * ii + ld_row_in;
+            const int row = w * kRowsPerWaveKv + kRPL * ii + ld_row_in;
             // rows past the end re-read the last query; their lse is +inf, so p = 0
             const uint32_t back = (row > rmax) ? (uint32_t)((row - rmax) * qstride * 2) : 0u;
-            load_lds16(qr, qoff[ii] - back, st + (w * kRowsPerWaveKv + 4 * ii) * kRowBytes);
-            load_lds16(gr, qoff[ii] - back, st + kTileBytes + (w * kRowsPerWaveKv + 4 * ii) * kRowBytes);
+            load_lds16(qr, qoff[ii] - back, st + (w * kRowsPerWaveKv + kRPL * ii) * kRowBytes);
+            load_lds16(gr, qoff[ii] - back, st + kTileBytes + (w * kRowsPerWaveKv + kRPL * ii) * kRowBytes);
         }
     };
     // lse (log2 domain, +inf past the end or for rows with no visible key) and D of a step,
@@ -572,10 +595,10 @@ __global__ void __launch_bounds__(kThreadsKv, 1) block_bwd_dkdv_kernel(const Bwd
     }
     uint32_t off_r[kD / 16];
 #pragma unroll
-    for (int ks = 0; ks < kD / 16; ++ks) off_r[ks] = row_off(lane, ks);
+    for (int ks = 0; ks < kD / 16; ++ks) off_r[ks] = BG::row_off(lane, ks);
     TrOff off_t[kD / 32];
 #pragma unroll
-    for (int db = 0; db < kD / 32; ++db) off_t[db] = tr_off(lane, db);
+    for (int db = 0; db < kD / 32; ++db) off_t[db] = BG::tr_off(lane, db);
 
     LDS_AS char* st0 = (LDS_AS char*)lds_stage0;
     LDS_AS char* st1 = (LDS_AS char*)lds_stage1;
@@ -657,7 +680,7 @@ __global__ void __launch_bounds__(kThreadsKv, 1) block_bwd_dkdv_kernel(const Bwd
     // the two query halves' partial sums: the second-half waves hand theirs to the first-half
     // waves through LDS (one tensor at a time; each stage holds two waves' 16 KB)
     {
-        LDS_AS float* xch = (LDS_AS float*)((kg >> 1) ? lds_stage1 : lds_stage0) + (kg & 1) * (64 * 64);
+        LDS_AS float* xch = (LDS_AS float*)((kg >> 1) ? lds_stage1 : lds_stage0) + (kg & 1) * ((kD / 32) * 16 * 64);
         auto combine = [&](f32x16(&acc)[kD / 32]) {
             if (qhalf == 1) {
 #pragma unroll
@@ -702,6 +725,21 @@ __global__ void __launch_bounds__(kThreadsKv, 1) block_bwd_dkdv_kernel(const Bwd
         }
 }
 
+template <int D>
+hipError_t launch_head_dim(const BwdParams& p, hipStream_t stream) {
+    // launches of fewer than two blocks per CU split each tile's keys over two wave groups
+    if (p.n_qt * p.n_cols < 512)
+        hipLaunchKernelGGL((block_bwd_dq_kernel<D, 2>), dim3((unsigned)(p.n_qt * p.n_cols)), dim3(2 * kThreads), 0,
+                           stream, p);
+    else
+        hipLaunchKernelGGL((block_bwd_dq_kernel<D, 1>), dim3((unsigned)(p.n_qt * p.n_cols)), dim3(kThreads), 0,
+                           stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(block_bwd_dkdv_kernel<D>, dim3((unsigned)(p.n_kb * p.kv_cols)), dim3(kThreadsKv), 0, stream, p);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_block_bwd_bf16(const BlockBwdArgs& a, hipStream_t stream) {
@@ -736,15 +774,7 @@ hipError_t launch_block_bwd_bf16(const BlockBwdArgs& a, hipStream_t stream) {
     p.kv_xcd_cols = (p.kv_cols % 8 == 0) ? p.kv_cols / 8 : 0;
     p.write_dq = a.write_dq ? 1 : 0;
     p.write_dkv = a.write_dkv ? 1 : 0;
-    // launches of fewer than two blocks per CU split each tile's keys over two wave groups
-    if (p.n_qt * p.n_cols < 512)
-        hipLaunchKernelGGL(block_bwd_dq_kernel<2>, dim3((unsigned)(p.n_qt * p.n_cols)), dim3(2 * kThreads), 0, stream, p);
-    else
-        hipLaunchKernelGGL(block_bwd_dq_kernel<1>, dim3((unsigned)(p.n_qt * p.n_cols)), dim3(kThreads), 0, stream, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(block_bwd_dkdv_kernel, dim3((unsigned)(p.n_kb * p.kv_cols)), dim3(kThreadsKv), 0, stream, p);
-    return hipGetLastError();
+    return a.head_dim == 64 ? launch_head_dim<64>(p, stream) : launch_head_dim<128>(p, stream);
 }
 
 }  // namespace cpattn

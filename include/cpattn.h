@@ -291,8 +291,8 @@ cpattn_status_t cpattn_attn_bwd_delta(const float* out, const void* dout, cpattn
  *                WRITE_DQ on its first step, so no accumulator needs clearing.
  * dtype CPATTN_BF16: bf16 products with fp32 accumulation; p and ds are rounded to bf16
  * (RNE) before the products that use them.  CPATTN_F32: fp32 throughout.  head_dim 64 or
- * 128 (bf16: 128, and a Q row of heads_q * 128 elements at most 2^24).  seq_q == 0 or
- * seq_kv == 0 adds nothing.
+ * 128 for both dtypes (bf16: a Q row of heads_q * head_dim elements at most 2^24).  seq_q == 0
+ * or seq_kv == 0 adds nothing.
  * Errors: INVALID_ARG (also unknown flag bits), SHAPE, UNSUPPORTED as for cpattn_block_fwd.
  */
 cpattn_status_t cpattn_block_bwd(const void* q, const void* k, const void* v, const void* dout,

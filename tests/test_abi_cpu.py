@@ -214,7 +214,8 @@ def test_block_bwd_validation(lib):
     assert _bb(lib, scale=float("nan")) == INVALID
     assert _bb(lib, hq=6, hkv=4) == SHAPE and "multiple" in _err(lib)
     assert _bb(lib, d=96, dtype=0) == UNSUPPORTED
-    assert _bb(lib, d=64, dtype=1) == UNSUPPORTED  # bf16 backward is D=128 only
+    # bf16 with head_dim 64 passes the head-dim check (refused here only for the misaligned q)
+    assert _bb(lib, d=64, dtype=1, q=ctypes.c_void_p(0x1004)) == UNSUPPORTED and "aligned" in _err(lib)
     # bf16 rows of Q (heads_q * head_dim) above 2^24 elements are refused
     assert _bb(lib, hq=(1 << 17) + 2, hkv=2) == UNSUPPORTED and "2^24" in _err(lib)
     for name in ("q", "k", "v", "dout", "qpos", "kvpos", "lse", "delta", "dq", "dk", "dv"):
