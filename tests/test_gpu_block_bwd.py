@@ -22,7 +22,7 @@ import torch
 
 import context_causal_attention_amd as cp
 import oracle
-from context_causal_attention_amd.workloads import WORKLOADS
+from context_causal_attention_amd.workloads import WORKLOADS, Workload
 from helpers import gen, max_abs, sample_rows, zigzag_chunks
 
 pytestmark = pytest.mark.gpu
@@ -256,6 +256,13 @@ def _ring_bwd_check(w, rows_per_chunk, key_samples, exact_forward):
 
 def test_ring_share_bwd_8k():
     _ring_bwd_check(WORKLOADS["rank_share_8k"], rows_per_chunk=12, key_samples=12, exact_forward=True)
+
+
+def test_ring_share_bwd_head_dim_64():
+    """The ring-share backward through the binding with bf16 and head dim 64: a zigzag rank's
+    share (S = 2048, C = 4, rank 1, 8 query / 2 K/V heads), every step's block backward."""
+    w = Workload("ring_bwd_d64", "ring_share", 1, 2048, 8, 2, 64, "bf16", 4, rank=1)
+    _ring_bwd_check(w, rows_per_chunk=12, key_samples=12, exact_forward=True)
 
 
 def test_ring_share_bwd_256k_sampled():
