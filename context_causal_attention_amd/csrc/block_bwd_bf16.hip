@@ -123,6 +123,18 @@ __device__ inline f32x16 mfma(const bf16x8& a, const bf16x8& b, const f32x16& c)
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Masking after the fact on a partly visible tile.  The weights are computed for every pair
+// of the tile and packed to bf16 two per register (element 2m in the low half, 2m + 1 in the
+// high half); a hidden pair's weight may be anything, inf or NaN included, and its 16 bits are
+// replaced whole by +0, so the products see exactly what a weight of 0 would give.  n is how
+// many of the register's two elements are kept, counted from the low half (keep_low) or from
+// the high half (keep_high); any n outside 0..2 is clamped.
+__device__ inline uint32_t keep_low(int n) { return n >= 2 ? 0xFFFFFFFFu : (n == 1 ? 0x0000FFFFu : 0u); }
+__device__ inline uint32_t keep_high(int n) { return n >= 2 ? 0xFFFFFFFFu : (n == 1 ? 0xFFFF0000u : 0u); }
+__device__ inline bf16x8 and_mask(const bf16x8& x, const u32x4& m) {
+    return __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, x) & m);
+}
+
 // Scheduling hint for a loop of N steps, each of M matrix-core products fed by R LDS reads:
 // issue the reads A steps ahead of the products that use them (sync group G).
 template <int N, int M, int R, int G, int A = 2>
@@ -253,6 +265,8 @@ __global__ void __launch_bounds__(64 * kNW * KS, 1) block_bwd_dq_kernel(const Bw
         n_ne += red[i];
         n_full += red[NW + i];
     }
+    n_ne = __builtin_amdgcn_readfirstlane(n_ne);  // the same in every lane: scalar registers
+    n_full = __builtin_amdgcn_readfirstlane(n_full);
 
     // K/V tile loads (both tensors row-read, same swizzle)
     const int64_t kvstride = (int64_t)p.heads_kv * kD;
@@ -356,19 +370,35 @@ __global__ void __launch_bounds__(64 * kNW * KS, 1) block_bwd_dq_kernel(const Bw
         sched_reads_ahead<8 * NKB, 2, 2, 1>();
 
         // ds = p (dp - D); entry v of key block kb is key 32*kb + 8*(v/4) + 4*half + v%4
-        const bool masked = jt >= n_full;
-        const int64_t rel = vis - (int64_t)jt * kTile - 4 * half;
-        const int lim = rel < 0 ? 0 : (rel > kTile ? kTile : (int)rel);
         bf16x8 dsb[NKB][2];
 #pragma unroll
         for (int kk = 0; kk < NKB; ++kk)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int kb = khalf * NKB + kk;
-                float pv = __builtin_amdgcn_exp2f(fmaf(s[kk][v], p.c, -lse2));
-                if (masked && 32 * kb + 8 * (v / 4) + v % 4 >= lim) pv = 0.f;
+                const float pv = __builtin_amdgcn_exp2f(fmaf(s[kk][v], p.c, -lse2));
                 dsb[kk][v >> 3][v & 7] = (__bf16)(pv * (dp[kk][v] - dlt));
             }
+        // A partly visible tile (a uniform branch, taken by few tiles): the row sees keys below
+        // lim of the tile, so each packed pair keeps lim - (its first key) elements from its low
+        // half.  Masking here rather than per weight keeps the compares and selects out of the
+        // other tiles.
+        if (jt >= n_full) {
+            // an empty volatile statement: the branch cannot be turned into selects executed
+            // on every tile
+            asm volatile("");
+            const int64_t rel = vis - (int64_t)jt * kTile - 4 * half;
+            const int lim = rel < 0 ? 0 : (rel > kTile ? kTile : (int)rel);
+#pragma unroll
+            for (int kk = 0; kk < NKB; ++kk)
+#pragma unroll
+                for (int h8 = 0; h8 < 2; ++h8) {
+                    // element 2m of dsb[kk][h8] is entry v = 8*h8 + 2m
+                    const int kfirst = 32 * (khalf * NKB + kk) + 16 * h8;
+                    const u32x4 m = {keep_low(lim - kfirst), keep_low(lim - kfirst - 2),
+                                     keep_low(lim - kfirst - 8), keep_low(lim - kfirst - 10)};
+                    dsb[kk][h8] = and_mask(dsb[kk][h8], m);
+                }
+        }
 
         // dQ^T += K^T dS^T
 #pragma unroll
@@ -502,6 +532,8 @@ __global__ void __launch_bounds__(kThreadsKv, 1) block_bwd_dkdv_kernel(const Bwd
         qt_lo += red[ii];
         qt_full += red[kNWkv + ii];
     }
+    qt_lo = __builtin_amdgcn_readfirstlane(qt_lo);  // the same in every lane: scalar registers
+    qt_full = __builtin_amdgcn_readfirstlane(qt_full);
     const int nq_vis = (int)n_qt - qt_lo;
     const int n_steps = nq_vis > 0 ? nq_vis * p.ratio : 0;  // (query head, query tile) pairs
     const int64_t h0 = (int64_t)kvh * p.ratio;
@@ -630,8 +662,6 @@ __global__ void __launch_bounds__(kThreadsKv, 1) block_bwd_dkdv_kernel(const Bwd
             }
             sched_reads_ahead<8, 2, 3, 3>();
             // entry v is query row qb*32 + 8*(v/4) + 4*half + v%4 of the tile, key l32
-            const int64_t rel = first - qt * kTile - qb * 32 - 4 * half;
-            const int lim = rel < 0 ? 0 : (rel > 32 ? 32 : (int)rel);
             bf16x8 pb[2], dsb[2];
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
@@ -641,10 +671,26 @@ __global__ void __launch_bounds__(kThreadsKv, 1) block_bwd_dkdv_kernel(const Bwd
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int v = 4 * g + e;
-                    float pv = __builtin_amdgcn_exp2f(fmaf(s[v], p.c, -lv[e]));
-                    if (masked && 8 * g + e < lim) pv = 0.f;
+                    const float pv = __builtin_amdgcn_exp2f(fmaf(s[v], p.c, -lv[e]));
                     pb[v >> 3][v & 7] = (__bf16)pv;
                     dsb[v >> 3][v & 7] = (__bf16)(pv * (dp[v] - dv4[e]));
+                }
+            }
+            // A partly visible tile (a uniform branch, taken by few steps): rows below lim of
+            // this half do not see the key, so each packed pair keeps (its first row) + 2 - lim
+            // elements from its high half.  Masking here rather than per weight keeps the
+            // compares and selects out of the other steps.
+            if (masked) {
+                asm volatile("");  // keeps the branch a branch (see the dq kernel)
+                const int64_t rel = first - qt * kTile - qb * 32 - 4 * half;
+                const int lim = rel < 0 ? 0 : (rel > 32 ? 32 : (int)rel);
+#pragma unroll
+                for (int h8 = 0; h8 < 2; ++h8) {
+                    // element 2m of pb[h8] and dsb[h8] is entry v = 8*h8 + 2m
+                    const int r = 16 * h8 + 2 - lim;
+                    const u32x4 m = {keep_high(r), keep_high(r + 2), keep_high(r + 8), keep_high(r + 10)};
+                    pb[h8] = and_mask(pb[h8], m);
+                    dsb[h8] = and_mask(dsb[h8], m);
                 }
             }
             // dV^T += dO^T P and dK^T += Q^T dS
