@@ -136,10 +136,11 @@ __device__ inline bf16x8 and_mask(const bf16x8& x, const u32x4& m) {
 }
 
 // Scheduling hint for a loop of N steps, each of M matrix-core products fed by R LDS reads:
-// issue the reads A steps ahead of the products that use them (sync group G).
-template <int N, int M, int R, int G, int A = 2>
+// issue the reads A steps ahead of the products that use them (sync group G).  X more LDS
+// reads, which the first products need, go out with the first group.
+template <int N, int M, int R, int G, int A = 2, int X = 0>
 __device__ inline void sched_reads_ahead() {
-    __builtin_amdgcn_sched_group_barrier(0x100, R * A, G);
+    __builtin_amdgcn_sched_group_barrier(0x100, R * A + X, G);
 #pragma unroll
     for (int i = 0; i < N - A; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, M, G);
@@ -599,7 +600,7 @@ __global__ void __launch_bounds__(kThreadsKv, 1) block_bwd_dkdv_kernel(const Bwd
             load_lds16(gr, qoff[ii] - back, st + kTileBytes + (w * kRowsPerWaveKv + kRPL * ii) * kRowBytes);
         }
     };
-    // lse (log2 domain, +inf past the end or for rows with no visible key) and D of a step,
+    // lse (log2 domain, +inf past the end or for rows with no visible key) and -D of a step,
     // one value per thread of the first two waves, fetched a step ahead through registers.
     // The raw value is converted only when it is stored at the end of the step, so that the
     // wave does not wait for the load (and the tile loads issued before it) at the start.
@@ -615,7 +616,7 @@ __global__ void __launch_bounds__(kThreadsKv, 1) block_bwd_dkdv_kernel(const Bwd
         return (row < p.seq_q) ? p.delta[li] : 0.f;
     };
     auto store_rowvals = [&](LDS_AS char* st, float x) {
-        if (w == 0) x = (x == -INFINITY) ? INFINITY : x * kLog2e;
+        x = (w == 0) ? ((x == -INFINITY) ? INFINITY : x * kLog2e) : -x;
         if (w < 2) ((LDS_AS float*)(st + 2 * kTileBytes))[tid] = x;
     };
 
@@ -650,8 +651,16 @@ __global__ void __launch_bounds__(kThreadsKv, 1) block_bwd_dkdv_kernel(const Bwd
         const bool masked = qt < qt_full;
         {
             const int qb = qhalf;
-            // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys
-            f32x16 s = f32x16{}, dp = f32x16{};
+            // S = Q K^T and dP - D = dO V^T - D for 32 queries x this wave's 32 keys: the dP
+            // products accumulate onto -D of each accumulator row (entry v is query row
+            // qb*32 + 8*(v/4) + 4*half + v%4 of the tile, key l32), so no subtraction follows
+            f32x16 s = f32x16{}, dp;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const f32x4 nd = *(const LDS_AS f32x4*)(dlt_l + qb * 32 + 8 * g + 4 * half);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dp[4 * g + e] = nd[e];
+            }
 #pragma unroll
             for (int ks = 0; ks < kD / 16; ++ks) {
                 const bf16x8 qa = lds_b128(qt_l + qb * 32 * kRowBytes + off_r[ks]);
@@ -660,20 +669,17 @@ __global__ void __launch_bounds__(kThreadsKv, 1) block_bwd_dkdv_kernel(const Bwd
                 s = mfma(qa, kreg[ks], s);
                 dp = mfma(ga, va, dp);
             }
-            sched_reads_ahead<8, 2, 3, 3>();
-            // entry v is query row qb*32 + 8*(v/4) + 4*half + v%4 of the tile, key l32
+            sched_reads_ahead<8, 2, 3, 3, 2, 4>();
             bf16x8 pb[2], dsb[2];
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int r0 = qb * 32 + 8 * g + 4 * half;
-                const f32x4 lv = *(const LDS_AS f32x4*)(lse_l + r0);
-                const f32x4 dv4 = *(const LDS_AS f32x4*)(dlt_l + r0);
+                const f32x4 lv = *(const LDS_AS f32x4*)(lse_l + qb * 32 + 8 * g + 4 * half);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int v = 4 * g + e;
                     const float pv = __builtin_amdgcn_exp2f(fmaf(s[v], p.c, -lv[e]));
                     pb[v >> 3][v & 7] = (__bf16)pv;
-                    dsb[v >> 3][v & 7] = (__bf16)(pv * (dp[v] - dv4[e]));
+                    dsb[v >> 3][v & 7] = (__bf16)(pv * dp[v]);
                 }
             }
             // A partly visible tile (a uniform branch, taken by few steps): rows below lim of
