@@ -478,10 +478,12 @@ __global__ void __launch_bounds__(kThreadsKv, 1) block_bwd_dkdv_kernel(const Bwd
     constexpr int kStageBytes = 2 * kTileBytes + 2 * kTile * 4;  // [Q | dO | lse2 | D]
     static_assert(kRowsPerWaveKv % kRPL == 0, "whole loads per wave");
     constexpr int kLoadsKv = kRowsPerWaveKv / kRPL;
-    __shared__ __attribute__((aligned(16))) char lds_stage0[kStageBytes];
-    __shared__ __attribute__((aligned(16))) char lds_stage1[kStageBytes];
+    __shared__ __attribute__((aligned(256))) char lds_stage0[kStageBytes];
+    __shared__ __attribute__((aligned(256))) char lds_stage1[kStageBytes];
     __shared__ int red[2 * kNWkv];
-    __shared__ __attribute__((aligned(16))) char lds_v[4 * 32 * kRowBytes];  // the block's V rows
+    // the block's V rows, key group g at rows 32*(g+1): the 32 rows of slack in front keep the
+    // read base below (shifted back by the wave's query-half offset) inside the array
+    __shared__ __attribute__((aligned(16))) char lds_v[5 * 32 * kRowBytes];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -548,7 +550,7 @@ __global__ void __launch_bounds__(kThreadsKv, 1) block_bwd_dkdv_kernel(const Bwd
     for (int ks = 0; ks < kD / 16; ++ks) kreg[ks] = load_row16(p.k + krow * kD + 16 * ks + 8 * half, kvalid);
     // V rows go to LDS once (the first-half waves write their key group's rows) and are read
     // as the dP operand with the same swizzled row offsets as the Q and dO tiles
-    LDS_AS char* vl = (LDS_AS char*)lds_v + kg * 32 * kRowBytes;
+    LDS_AS char* vl = (LDS_AS char*)lds_v + (kg + 1) * 32 * kRowBytes;
     if (qhalf == 0) {
 #pragma unroll
         for (int ks = 0; ks < kD / 16; ++ks)
@@ -626,12 +628,21 @@ __global__ void __launch_bounds__(kThreadsKv, 1) block_bwd_dkdv_kernel(const Bwd
         dk[db] = f32x16{};
         dv[db] = f32x16{};
     }
+    // Operand offsets include the wave's query half (rows 32*qhalf of each staged tile), so the
+    // Q and dO reads address a stage, whose base is a constant, with no add in the loop; the V
+    // rows are read from a base shifted back by the same amount.
+    const uint32_t qbase = (uint32_t)(qhalf * 32 * kRowBytes);
     uint32_t off_r[kD / 16];
 #pragma unroll
-    for (int ks = 0; ks < kD / 16; ++ks) off_r[ks] = BG::row_off(lane, ks);
+    for (int ks = 0; ks < kD / 16; ++ks) off_r[ks] = BG::row_off(lane, ks) + qbase;
     TrOff off_t[kD / 32];
 #pragma unroll
-    for (int db = 0; db < kD / 32; ++db) off_t[db] = BG::tr_off(lane, db);
+    for (int db = 0; db < kD / 32; ++db) {
+        off_t[db] = BG::tr_off(lane, db);
+        off_t[db].a += qbase;
+        off_t[db].b += qbase;
+    }
+    const LDS_AS char* vq = (const LDS_AS char*)lds_v + (kg + 1 - qhalf) * 32 * kRowBytes;
 
     LDS_AS char* st0 = (LDS_AS char*)lds_stage0;
     LDS_AS char* st1 = (LDS_AS char*)lds_stage1;
@@ -663,9 +674,9 @@ __global__ void __launch_bounds__(kThreadsKv, 1) block_bwd_dkdv_kernel(const Bwd
             }
 #pragma unroll
             for (int ks = 0; ks < kD / 16; ++ks) {
-                const bf16x8 qa = lds_b128(qt_l + qb * 32 * kRowBytes + off_r[ks]);
-                const bf16x8 ga = lds_b128(gt_l + qb * 32 * kRowBytes + off_r[ks]);
-                const bf16x8 va = lds_b128(vl + off_r[ks]);
+                const bf16x8 qa = lds_b128(qt_l + off_r[ks]);
+                const bf16x8 ga = lds_b128(gt_l + off_r[ks]);
+                const bf16x8 va = lds_b128(vq + off_r[ks]);
                 s = mfma(qa, kreg[ks], s);
                 dp = mfma(ga, va, dp);
             }
@@ -704,7 +715,7 @@ __global__ void __launch_bounds__(kThreadsKv, 1) block_bwd_dkdv_kernel(const Bwd
             for (int db = 0; db < kD / 32; ++db)
 #pragma unroll
                 for (int ks2 = 0; ks2 < 2; ++ks2) {
-                    const int rb = (qb * 32 + 16 * ks2) * kRowBytes;
+                    const int rb = 16 * ks2 * kRowBytes;
                     const bf16x8 ga = lds_tr_pair(gt_l + rb + off_t[db].a, gt_l + rb + off_t[db].b);
                     const bf16x8 qa = lds_tr_pair(qt_l + rb + off_t[db].a, qt_l + rb + off_t[db].b);
                     dv[db] = mfma(ga, pb[ks2], dv[db]);
