@@ -14,9 +14,10 @@
 //
 // dq kernel: a block of 4 waves owns G query heads sharing one K/V head times 128/G query
 // positions; each lane holds one query row (its q and dout as matrix operands).  K/V tiles
-// of 64 keys are staged in LDS (direct global->LDS loads, two stages).  Per tile:
-//   S^T = K Q^T and dP^T = V dO^T (K, V rows read from LDS), p and ds per lane (one query:
-//   lse and D are per-lane scalars), dQ^T += K^T dS^T (K read transposed, ds_read_b64_tr_b16).
+// of 64 keys are staged in LDS (direct global->LDS loads, two stages).  Per 32-key block of a
+// tile: S^T = K Q^T and dP^T - D = V dO^T - D (K, V rows read from LDS; the products start from
+// -D), p and ds per lane (one query: lse and D are per-lane scalars), dQ^T += K^T dS^T (K read
+// transposed, ds_read_b64_tr_b16).
 //   Launches too small to fill the chip take 8 waves instead, two per 32-row query group, each
 //   over one 32-key half of every tile (block_bwd_dq_kernel<2>).
 // dk/dv kernel: a block of 8 waves owns 128 keys of one K/V head, in 4 groups of 32 (one key
@@ -320,6 +321,9 @@ __global__ void __launch_bounds__(64 * kNW * KS, 1) block_bwd_dq_kernel(const Bw
     // a row with no visible key anywhere has lse = -inf and every pair masked
     const float lse2 = (lse_v == -INFINITY) ? INFINITY : lse_v * kLog2e;
     const float dlt = valid ? p.delta[li] : 0.f;
+    f32x16 ndlt;  // -D in every entry: the dP products accumulate onto it
+#pragma unroll
+    for (int v = 0; v < 16; ++v) ndlt[v] = -dlt;
 
     int64_t vis = 0;  // keys visible to this row, needed only when some tile is partly visible
     if (n_full < n_ne) {
@@ -350,70 +354,61 @@ __global__ void __launch_bounds__(64 * kNW * KS, 1) block_bwd_dq_kernel(const Bw
         const LDS_AS char* vt = kt + kTileBytes;
         if (jt + 1 < n_ne) issue_tile(jt + 1, nxt);
 
-        // S^T = K Q^T and dP^T = V dO^T for this wave's 32-key blocks of the tile (key block
-        // kb = khalf * NKB + kk)
-        f32x16 s[NKB], dp[NKB];
+        // The wave's 32-key blocks of the tile one after the other (key block kb = khalf * NKB
+        // + kk): S^T = K Q^T and dP^T - D = V dO^T - D (the products accumulate onto -D), ds,
+        // then dQ^T += K^T dS^T.  One block at a time leaves the registers for the -D operand
+        // (the subtraction per weight goes) and splits the vector work into shorter runs.
 #pragma unroll
         for (int kk = 0; kk < NKB; ++kk) {
-            s[kk] = f32x16{};
-            dp[kk] = f32x16{};
-        }
+            const int kb = khalf * NKB + kk;
+            f32x16 s = f32x16{}, dp = ndlt;
 #pragma unroll
-        for (int ks = 0; ks < kD / 16; ++ks)
-#pragma unroll
-            for (int kk = 0; kk < NKB; ++kk) {
-                const int kb = khalf * NKB + kk;
+            for (int ks = 0; ks < kD / 16; ++ks) {
                 const bf16x8 ka = lds_b128(kt + kb * 32 * kRowBytes + off_r[ks]);
                 const bf16x8 va = lds_b128(vt + kb * 32 * kRowBytes + off_r[ks]);
-                s[kk] = mfma(ka, qreg[ks], s[kk]);
-                dp[kk] = mfma(va, doreg[ks], dp[kk]);
+                s = mfma(ka, qreg[ks], s);
+                dp = mfma(va, doreg[ks], dp);
             }
-        sched_reads_ahead<8 * NKB, 2, 2, 1>();
+            sched_reads_ahead<8, 2, 2, 1>();
 
-        // ds = p (dp - D); entry v of key block kb is key 32*kb + 8*(v/4) + 4*half + v%4
-        bf16x8 dsb[NKB][2];
-#pragma unroll
-        for (int kk = 0; kk < NKB; ++kk)
+            // ds = p (dp - D); entry v is key 32*kb + 8*(v/4) + 4*half + v%4 of the tile
+            bf16x8 dsb[2];
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const float pv = __builtin_amdgcn_exp2f(fmaf(s[kk][v], p.c, -lse2));
-                dsb[kk][v >> 3][v & 7] = (__bf16)(pv * (dp[kk][v] - dlt));
+                const float pv = __builtin_amdgcn_exp2f(fmaf(s[v], p.c, -lse2));
+                dsb[v >> 3][v & 7] = (__bf16)(pv * dp[v]);
             }
-        // A partly visible tile (a uniform branch, taken by few tiles): the row sees keys below
-        // lim of the tile, so each packed pair keeps lim - (its first key) elements from its low
-        // half.  Masking here rather than per weight keeps the compares and selects out of the
-        // other tiles.
-        if (jt >= n_full) {
-            // an empty volatile statement: the branch cannot be turned into selects executed
-            // on every tile
-            asm volatile("");
-            const int64_t rel = vis - (int64_t)jt * kTile - 4 * half;
-            const int lim = rel < 0 ? 0 : (rel > kTile ? kTile : (int)rel);
-#pragma unroll
-            for (int kk = 0; kk < NKB; ++kk)
+            // A partly visible tile (a uniform branch, taken by few tiles): the row sees keys
+            // below lim of the tile, so each packed pair keeps lim - (its first key) elements
+            // from its low half.  Masking here rather than per weight keeps the compares and
+            // selects out of the other tiles.
+            if (jt >= n_full) {
+                // an empty volatile statement: the branch cannot be turned into selects
+                // executed on every tile
+                asm volatile("");
+                const int64_t rel = vis - (int64_t)jt * kTile - 4 * half;
+                const int lim = rel < 0 ? 0 : (rel > kTile ? kTile : (int)rel);
 #pragma unroll
                 for (int h8 = 0; h8 < 2; ++h8) {
-                    // element 2m of dsb[kk][h8] is entry v = 8*h8 + 2m
-                    const int kfirst = 32 * (khalf * NKB + kk) + 16 * h8;
+                    // element 2m of dsb[h8] is entry v = 8*h8 + 2m
+                    const int kfirst = 32 * kb + 16 * h8;
                     const u32x4 m = {keep_low(lim - kfirst), keep_low(lim - kfirst - 2),
                                      keep_low(lim - kfirst - 8), keep_low(lim - kfirst - 10)};
-                    dsb[kk][h8] = and_mask(dsb[kk][h8], m);
+                    dsb[h8] = and_mask(dsb[h8], m);
                 }
-        }
+            }
 
-        // dQ^T += K^T dS^T
+            // dQ^T += K^T dS^T
 #pragma unroll
-        for (int db = 0; db < kD / 32; ++db)
-#pragma unroll
-            for (int kk = 0; kk < NKB; ++kk)
+            for (int db = 0; db < kD / 32; ++db)
 #pragma unroll
                 for (int ks2 = 0; ks2 < 2; ++ks2) {
-                    const int kb = khalf * NKB + kk;
                     const LDS_AS char* base = kt + (32 * kb + 16 * ks2) * kRowBytes;
                     const bf16x8 a = lds_tr_pair(base + off_t[db].a, base + off_t[db].b);
-                    acc[db] = mfma(a, dsb[kk][ks2], acc[db]);
+                    acc[db] = mfma(a, dsb[ks2], acc[db]);
                 }
-        sched_reads_ahead<8 * NKB, 1, 2, 2>();
+            sched_reads_ahead<8, 1, 2, 2>();
+        }
 
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next tile has landed
         __syncthreads();
