@@ -138,15 +138,18 @@ __device__ inline bf16x8 and_mask(const bf16x8& x, const u32x4& m) {
 
 // Scheduling hint for a loop of N steps, each of M matrix-core products fed by R LDS reads:
 // issue the reads A steps ahead of the products that use them (sync group G).  X more LDS
-// reads, which the first products need, go out with the first group.
-template <int N, int M, int R, int G, int A = 2, int X = 0>
+// reads, which the first products need, go out with the first group, and Y more, which the
+// vector work after the products needs, with the last one.
+template <int N, int M, int R, int G, int A = 2, int X = 0, int Y = 0>
 __device__ inline void sched_reads_ahead() {
     __builtin_amdgcn_sched_group_barrier(0x100, R * A + X, G);
 #pragma unroll
-    for (int i = 0; i < N - A; ++i) {
+    for (int i = 0; i < N - A - 1; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, M, G);
         __builtin_amdgcn_sched_group_barrier(0x100, R, G);
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, M, G);
+    __builtin_amdgcn_sched_group_barrier(0x100, R + Y, G);
     __builtin_amdgcn_sched_group_barrier(0x008, M * A, G);
 }
 
@@ -667,6 +670,7 @@ __global__ void __launch_bounds__(kThreadsKv, 1) block_bwd_dkdv_kernel(const Bwd
 #pragma unroll
                 for (int e = 0; e < 4; ++e) dp[4 * g + e] = nd[e];
             }
+            f32x4 lv[4];
 #pragma unroll
             for (int ks = 0; ks < kD / 16; ++ks) {
                 const bf16x8 qa = lds_b128(qt_l + off_r[ks]);
@@ -674,16 +678,20 @@ __global__ void __launch_bounds__(kThreadsKv, 1) block_bwd_dkdv_kernel(const Bwd
                 const bf16x8 va = lds_b128(vq + off_r[ks]);
                 s = mfma(qa, kreg[ks], s);
                 dp = mfma(ga, va, dp);
+                if (ks == kD / 16 - 1) {
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) lv[g] = *(const LDS_AS f32x4*)(lse_l + qb * 32 + 8 * g + 4 * half);
+                }
             }
-            sched_reads_ahead<8, 2, 3, 3, 2, 4>();
+            // the row values go out with the last operand reads, ahead of the final products
+            sched_reads_ahead<8, 2, 3, 3, 2, 4, 4>();
             bf16x8 pb[2], dsb[2];
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const f32x4 lv = *(const LDS_AS f32x4*)(lse_l + qb * 32 + 8 * g + 4 * half);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int v = 4 * g + e;
-                    const float pv = __builtin_amdgcn_exp2f(fmaf(s[v], p.c, -lv[e]));
+                    const float pv = __builtin_amdgcn_exp2f(fmaf(s[v], p.c, -lv[g][e]));
                     pb[v >> 3][v & 7] = (__bf16)pv;
                     dsb[v >> 3][v & 7] = (__bf16)(pv * dp[v]);
                 }
