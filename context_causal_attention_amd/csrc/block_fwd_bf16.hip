@@ -747,8 +747,8 @@ hipError_t launch_head_dim(const BlockFwdArgs& a, Params p, hipStream_t stream) 
         // softmax's vector work per score is the same as at 128 while the products per score
         // halve, so the kernel is bound by vector work, and a fourth wave per SIMD gives it
         // more to run beside (+2.8% on a 64K causal block, +4-7% on a 16K one).
-        if (D == 64) return launch_variant<D, 16, 1, 1, 1>(p, a.seq_q, stream);
-        return launch_variant<D, 12, 1, 1, 1>(p, a.seq_q, stream);
+        if constexpr (D == 64) return launch_variant<D, 16, 1, 1, 1>(p, a.seq_q, stream);
+        else return launch_variant<D, 12, 1, 1, 1>(p, a.seq_q, stream);
     }
     return launch_variant<D, 8, 1, 2, 1>(p, a.seq_q, stream);
 }
