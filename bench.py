@@ -71,8 +71,9 @@ def parse_args(argv=None):
                          "small workloads); the attention launches are then timed as part of the step")
     ap.add_argument("--extras", default=None,
                     help="comma-separated workload[:mode] list measured after the main line and reported "
-                         "under 'extra' (default: the Ulysses group in its explicit and its fused form and "
-                         "the per-step ring share when the main line is the default one; '' for none)")
+                         "under 'extra' (mode 'bwd': the workload's backward; default: the Ulysses group in "
+                         "its explicit and its fused form, the per-step ring share and the ring share's "
+                         "backward when the main line is the default one; '' for none)")
     ap.add_argument("--no-flush", action="store_true",
                     help="skip the bandwidth-bound kernels' separate timing under the MALL flush")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -655,12 +656,15 @@ def extra_line(name: str, mode: str, steps: int, warmup: int, dev):
     import torch
     from context_causal_attention_amd.workloads import WORKLOADS
     w = WORKLOADS[name]
-    plan = Plan(w, dev, mode=mode)
+    bwd = mode == "bwd"  # the workload's backward (its one-launch forward saved first), 10*D FLOPs per pair
+    plan = Plan(w, dev, mode="single" if bwd else mode, backward=bwd)
     m = measure(plan, steps, warmup)
-    res = {"workload": workload_name(w, mode, False, False), "steps": steps, "ms_per_step": round(m["ms_step"], 4),
+    res = {"workload": workload_name(w, "single" if bwd else mode, bwd, False), "steps": steps,
+           "ms_per_step": round(m["ms_step"], 4),
            "ms_per_step_median": round(m["ms_steps"][len(m["ms_steps"]) // 2], 4),
            "value": round(m["value"], 3), "unit": "TFLOP/s", "pct_of_bf16_peak": round(100.0 * m["value"] / PEAK_BF16_TFLOPS, 2),
-           "attention": {"kernel": "block_fwd_bf16", "achieved": round(m["achieved"], 3), "peak": PEAK_BF16_TFLOPS,
+           "attention": {"kernel": "block_bwd_dq_kernel+block_bwd_dkdv_kernel" if bwd else "block_fwd_bf16",
+                         "achieved": round(m["achieved"], 3), "peak": PEAK_BF16_TFLOPS,
                          "frac": round(m["achieved"] / PEAK_BF16_TFLOPS, 4),
                          "avg_launch_ms": round(sum(m["attn_ms"]) / len(m["attn_ms"]), 4), "launches": len(m["attn_ms"])},
            "hbm_kernels": m["hbm_kernels"], "hbm_kernels_flushed": hbm_flushed(plan),
@@ -764,10 +768,12 @@ def main(argv=None) -> int:
 # Measured beside the default line, in the same run: the Ulysses group with the workload's
 # explicit permute, attention and inverse permute ("On Context Parallelism", All-to-all); the
 # same group as the library's Ulysses share runs it, the exchanges folded into the attention's
-# row addressing; and the long-context ring share in its per-step form, one attention launch
-# per ring step into a tile and the merge kernel after each ("On Context Parallelism",
-# Peer-to-peer / Forward).
-EXTRAS = [("ulysses_gqa_128k", "single"), ("ulysses_gqa_128k", "fused"), ("ring_share_256k", "unfused")]
+# row addressing; the long-context ring share in its per-step form, one attention launch per
+# ring step into a tile and the merge kernel after each ("On Context Parallelism",
+# Peer-to-peer / Forward); and that share's backward, delta once and one dq and one dk/dv
+# launch per ring step ("On Context Parallelism", Peer-to-peer / Backward).
+EXTRAS = [("ulysses_gqa_128k", "single"), ("ulysses_gqa_128k", "fused"), ("ring_share_256k", "unfused"),
+          ("ring_share_256k", "bwd")]
 
 
 if __name__ == "__main__":
