@@ -54,8 +54,9 @@ def parse_args(argv=None):
     ap.add_argument("--workload", default="ring_share_256k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
-                    help="bwd: time the ring-share backward (delta + one block backward per ring "
-                         "step) instead of the forward; ring_share workloads only")
+                    help="bwd: time the ring-share backward (delta + cpattn_ring_share_bwd; with "
+                         "--mode unfused, one cpattn_block_bwd per ring step) instead of the forward; "
+                         "ring_share workloads only")
     ap.add_argument("--mode", choices=("single", "fused", "unfused"), default="single",
                     help="ring share: one launch over all ring blocks (single), one launch per step "
                          "merging in its epilogue (fused), or per-step tiles plus the merge kernel "
@@ -213,6 +214,12 @@ class Plan:
             # algorithmic backward FLOPs: 10*D per visible pair and query head (S = QK^T
             # recomputed, dP = dO V^T, dV = P^T dO, dQ = dS K, dK = dS^T Q)
             self.attn_flops = [f * 2.5 for f in self.attn_flops]
+            # "unfused": one cpattn_block_bwd per ring step; otherwise the share's one
+            # cpattn_ring_share_bwd call (dq per step, one dk/dv launch over all blocks), timed
+            # as one unit
+            self.bwd_steps = mode == "unfused"
+            if not self.bwd_steps:
+                self.attn_flops = [sum(self.attn_flops)]
             self.backward = True
         self.flops = sum(self.attn_flops)
         self.hbm_ev = []  # (kernel, bytes, start, end) of the timed steps' bandwidth-bound kernels
@@ -331,8 +338,9 @@ class Plan:
         return calls
 
     def step_bwd(self, ev=None):
-        """One rank share of the ring backward: delta, then the block backward of each ring
-        step (dq written at step 0 and added after; each owner's dk, dv written by its step)."""
+        """One rank share of the ring backward: delta, then the share's backward in one call
+        (cpattn_ring_share_bwd), or ("unfused") the block backward of each ring step (dq
+        written at step 0 and added after; each owner's dk, dv written by its step)."""
         cp, torch, w = self.cp, self.torch, self.w
         C, r = w.cp_size, w.rank
         nb = self.out.numel() * 4 + self.dout.numel() * self.dout.element_size() + self.delta.numel() * 4
@@ -345,6 +353,20 @@ class Plan:
         else:
             cp.attn_bwd_delta(self.out, self.dout, self.delta)
         q = self.qs[r]
+        if not self.bwd_steps:
+            order = [(r - step) % C for step in range(C)]
+            a = (q, self.dout, [self.k[o] for o in order], [self.v[o] for o in order], [self.pos[o] for o in order],
+                 self.pos[r], w.scale, self.lse, self.delta, self.dq, [self.dks[o] for o in order],
+                 [self.dvs[o] for o in order])
+            if ev is not None:
+                s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                s.record()
+                cp.ring_blocks_bwd(*a)
+                e.record()
+                ev.append((s, e))
+            else:
+                cp.ring_blocks_bwd(*a)
+            return
         for step in range(C):
             owner = (r - step) % C
             flags = cp.BWD_WRITE_DKV | (cp.BWD_WRITE_DQ if step == 0 else 0)

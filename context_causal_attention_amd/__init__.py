@@ -23,6 +23,7 @@ from ._binding import (  # noqa: F401
     load_library,
     lse_merge,
     reorder_gathered,
+    ring_blocks_bwd,
     ring_blocks_fwd,
     ring_share_bwd,
     ring_share_fwd,

@@ -62,12 +62,14 @@ def load_library():
     L.cpattn_attn_bwd_delta.argtypes = [P, P, ctypes.c_int, i32, i64, i32, i32, P, P]
     L.cpattn_block_bwd.argtypes = [P, P, P, P, ctypes.c_int, i32, i64, i64, i32, i32, i32, P, P, f32, P, P, P,
                                    P, P, ctypes.c_uint32, P]
+    L.cpattn_ring_share_bwd.argtypes = [P, P, P, P, P, P, i32, ctypes.c_int, i32, i64, i32, i32, i32, P, f32, P, P,
+                                        P, P, P, P]
     L.cpattn_reorder_gathered.argtypes = [P, P, i32, i64, i64, i32, ctypes.c_int, P]
     L.cpattn_ulysses_permute.argtypes = [P, P, i32, i32, i64, i32, i32, i32, i32, ctypes.c_int, P]
     L.cpattn_ulysses_permute_zigzag.argtypes = list(L.cpattn_ulysses_permute.argtypes)
     for name in ("cpattn_zigzag_index", "cpattn_zigzag_index_all", "cpattn_block_fwd", "cpattn_block_fwd_merge", "cpattn_block_fwd_rows",
                  "cpattn_lse_merge",
-                 "cpattn_attn_bwd_delta", "cpattn_block_bwd", "cpattn_ring_share_fwd",
+                 "cpattn_attn_bwd_delta", "cpattn_block_bwd", "cpattn_ring_share_fwd", "cpattn_ring_share_bwd",
                  "cpattn_reorder_gathered", "cpattn_ulysses_permute", "cpattn_ulysses_permute_zigzag"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
@@ -462,14 +464,48 @@ def block_bwd(q, k, v, dout, q_pos, kv_pos, scale: float, lse, delta, dq, dk, dv
     return dq, dk, dv
 
 
+def ring_blocks_bwd(q, dout, k_blocks, v_blocks, kv_positions, q_pos, scale: float, lse, delta, dq, dk_blocks,
+                    dv_blocks):
+    """The backward against K/V blocks in one call (cpattn_ring_share_bwd): dq written with the
+    sum over the blocks, dk_blocks[o] and dv_blocks[o] written with block o's parts."""
+    L = load_library()
+    n = len(k_blocks)
+    if not (len(v_blocks) == len(kv_positions) == len(dk_blocks) == len(dv_blocks) == n):
+        raise ValueError("the block lists must have the same length")
+    B, Sq, Hq, D = q.shape
+    _need(q, "q")
+    _need(dout, "dout", q.dtype, (B, Sq, Hq, D))
+    _need(q_pos, "q_pos", torch.int64, (Sq,))
+    _need(lse, "lse", torch.float32, (B, Hq, Sq))
+    _need(delta, "delta", torch.float32, (B, Hq, Sq))
+    _need(dq, "dq", torch.float32, (B, Sq, Hq, D))
+    Hkv = k_blocks[0].shape[2]
+    for o in range(n):
+        So = k_blocks[o].shape[1]
+        _need(k_blocks[o], f"k_blocks[{o}]", q.dtype, (B, So, Hkv, D))
+        _need(v_blocks[o], f"v_blocks[{o}]", q.dtype, (B, So, Hkv, D))
+        _need(kv_positions[o], f"kv_positions[{o}]", torch.int64, (So,))
+        _need(dk_blocks[o], f"dk_blocks[{o}]", torch.float32, (B, So, Hkv, D))
+        _need(dv_blocks[o], f"dv_blocks[{o}]", torch.float32, (B, So, Hkv, D))
+    arr = lambda ts: (ctypes.c_void_p * n)(*[t.data_ptr() for t in ts])  # noqa: E731
+    sq = (ctypes.c_int64 * n)(*[t.shape[1] for t in k_blocks])
+    dt = CPATTN_BF16 if q.dtype == torch.bfloat16 else CPATTN_F32
+    _check(L.cpattn_ring_share_bwd(_ptr(q), _ptr(dout), arr(k_blocks), arr(v_blocks), arr(kv_positions), sq, n, dt, B,
+                                   Sq, Hq, Hkv, D, _ptr(q_pos), float(scale), _ptr(lse), _ptr(delta), _ptr(dq),
+                                   arr(dk_blocks), arr(dv_blocks), _stream(q.device)))
+    return dq, dk_blocks, dv_blocks
+
+
 def ring_share_bwd(q, k_blocks, v_blocks, positions, rank: int, scale: float, out, lse, dout,
-                   dq=None, dk_blocks=None, dv_blocks=None):
+                   dq=None, dk_blocks=None, dv_blocks=None, mode: str = "single"):
     """Rank ``rank``'s share of the ring backward ("On Context Parallelism", Peer-to-peer /
     Backward): delta once, then for each step the block backward against owner
     (rank - step) mod C's K/V; dq adds up over the steps, and owner o's dk and dv
     contributions go into ``dk_blocks[o]``, ``dv_blocks[o]`` (the buffers that travel with
     its K/V on a ring).  Step 0 writes dq and each owner's dk, dv are written by its one step,
-    so nothing needs clearing first.  Returns (dq, dk_blocks, dv_blocks)."""
+    so nothing needs clearing first.  ``mode``: "single" (cpattn_ring_share_bwd: the dq
+    launches per step and one dk/dv launch over all blocks) or "steps" (cpattn_block_bwd per
+    step); both give the same bits.  Returns (dq, dk_blocks, dv_blocks)."""
     C = len(k_blocks)
     B, s, Hq, D = q.shape
     if dq is None:
@@ -479,8 +515,15 @@ def ring_share_bwd(q, k_blocks, v_blocks, positions, rank: int, scale: float, ou
     if dv_blocks is None:
         dv_blocks = [torch.empty(v.shape, dtype=torch.float32, device=q.device) for v in v_blocks]
     delta = attn_bwd_delta(out, dout)
-    for step in range(C):
-        owner = (rank - step) % C
+    order = [(rank - step) % C for step in range(C)]
+    if mode == "single":
+        ring_blocks_bwd(q, dout, [k_blocks[o] for o in order], [v_blocks[o] for o in order],
+                        [positions[o] for o in order], positions[rank], scale, lse, delta, dq,
+                        [dk_blocks[o] for o in order], [dv_blocks[o] for o in order])
+        return dq, dk_blocks, dv_blocks
+    if mode != "steps":
+        raise ValueError(f"unknown mode {mode!r}")
+    for step, owner in enumerate(order):
         flags = BWD_WRITE_DKV | (BWD_WRITE_DQ if step == 0 else 0)
         block_bwd(q, k_blocks[owner], v_blocks[owner], dout, positions[rank], positions[owner], scale, lse,
                   delta, dq, dk_blocks[owner], dv_blocks[owner], flags)

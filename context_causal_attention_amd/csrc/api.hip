@@ -6,6 +6,8 @@
 #include "cpattn_internal.h"
 
 #include <math.h>
+
+#include <algorithm>
 #include <stdarg.h>
 #include <stdio.h>
 
@@ -257,16 +259,14 @@ CPATTN_API cpattn_status_t cpattn_attn_bwd_delta(const float* out, const void* d
                     "attn_bwd_delta");
 }
 
-CPATTN_API cpattn_status_t cpattn_block_bwd(const void* q, const void* k, const void* v, const void* dout,
-                                            cpattn_dtype_t dtype, int32_t batch, int64_t seq_q, int64_t seq_kv,
-                                            int32_t heads_q, int32_t heads_kv, int32_t head_dim,
-                                            const int64_t* q_positions, const int64_t* kv_positions,
-                                            float scale, const float* lse, const float* delta, float* dq,
-                                            float* dk, float* dv, uint32_t flags, void* stream) {
-    const char* name = "block_bwd";
-    if (flags & ~(uint32_t)(CPATTN_BWD_WRITE_DQ | CPATTN_BWD_WRITE_DKV))
-        return fail(CPATTN_ERR_INVALID_ARG, "%s: unknown flags 0x%x", name, flags);
-    const bool wdq = (flags & CPATTN_BWD_WRITE_DQ) != 0, wdkv = (flags & CPATTN_BWD_WRITE_DKV) != 0;
+// Validation of one block's backward call, enqueueing nothing.  *empty: no (query, key) pair
+// (seq_q == 0 or seq_kv == 0), when only the accumulators to overwrite are touched (zeroed).
+static cpattn_status_t block_bwd_check(const char* name, const void* q, const void* k, const void* v,
+                                       const void* dout, cpattn_dtype_t dtype, int32_t batch, int64_t seq_q,
+                                       int64_t seq_kv, int32_t heads_q, int32_t heads_kv, int32_t head_dim,
+                                       const int64_t* q_positions, const int64_t* kv_positions, float scale,
+                                       const float* lse, const float* delta, const float* dq, const float* dk,
+                                       const float* dv, bool wdq, bool wdkv, bool* empty) {
     if (dtype != CPATTN_F32 && dtype != CPATTN_BF16)
         return fail(CPATTN_ERR_INVALID_ARG, "%s: unknown dtype %d", name, (int)dtype);
     if (batch <= 0 || heads_q <= 0 || heads_kv <= 0)
@@ -282,21 +282,10 @@ CPATTN_API cpattn_status_t cpattn_block_bwd(const void* q, const void* k, const 
     if (dtype == CPATTN_BF16 && (int64_t)heads_q * head_dim > kMaxRowElems)
         return fail(CPATTN_ERR_UNSUPPORTED, "%s: heads_q * head_dim = %lld above 2^24", name,
                     (long long)heads_q * head_dim);
-    if (seq_q == 0 || seq_kv == 0) {
-        // no pair: nothing to add; accumulators to overwrite become zero
-        if (wdq && seq_q > 0) {
-            if (!dq) return fail(CPATTN_ERR_INVALID_ARG, "%s: NULL pointer", name);
-            const hipError_t e = cpattn::launch_zero_fill(dq, (int64_t)batch * seq_q * heads_q * head_dim,
-                                                          (hipStream_t)stream);
-            if (e != hipSuccess) return from_hip(e, name);
-        }
-        if (wdkv && seq_kv > 0) {
-            if (!dk || !dv) return fail(CPATTN_ERR_INVALID_ARG, "%s: NULL pointer", name);
-            const int64_t n = (int64_t)batch * seq_kv * heads_kv * head_dim;
-            hipError_t e = cpattn::launch_zero_fill(dk, n, (hipStream_t)stream);
-            if (e == hipSuccess) e = cpattn::launch_zero_fill(dv, n, (hipStream_t)stream);
-            if (e != hipSuccess) return from_hip(e, name);
-        }
+    *empty = (seq_q == 0 || seq_kv == 0);
+    if (*empty) {
+        if ((wdq && seq_q > 0 && !dq) || (wdkv && seq_kv > 0 && (!dk || !dv)))
+            return fail(CPATTN_ERR_INVALID_ARG, "%s: NULL pointer", name);
         return ok();
     }
     if (!q || !k || !v || !dout || !q_positions || !kv_positions || !lse || !delta || !dq || !dk || !dv)
@@ -307,11 +296,110 @@ CPATTN_API cpattn_status_t cpattn_block_bwd(const void* q, const void* k, const 
     if ((seq_q + 31) / 32 * (int64_t)batch * heads_q > kMaxGrid ||
         (seq_kv + 31) / 32 * (int64_t)batch * heads_kv > kMaxGrid || heads_q > 65535 || batch > 65535)
         return fail(CPATTN_ERR_UNSUPPORTED, "%s: launch grid too large", name);
+    return ok();
+}
+
+// A call without pairs: the accumulators to overwrite become zero.
+static cpattn_status_t block_bwd_empty(const char* name, int32_t batch, int64_t seq_q, int64_t seq_kv,
+                                       int32_t heads_q, int32_t heads_kv, int32_t head_dim, float* dq, float* dk,
+                                       float* dv, bool wdq, bool wdkv, void* stream) {
+    if (wdq && seq_q > 0) {
+        const hipError_t e =
+            cpattn::launch_zero_fill(dq, (int64_t)batch * seq_q * heads_q * head_dim, (hipStream_t)stream);
+        if (e != hipSuccess) return from_hip(e, name);
+    }
+    if (wdkv && seq_kv > 0) {
+        const int64_t n = (int64_t)batch * seq_kv * heads_kv * head_dim;
+        hipError_t e = cpattn::launch_zero_fill(dk, n, (hipStream_t)stream);
+        if (e == hipSuccess) e = cpattn::launch_zero_fill(dv, n, (hipStream_t)stream);
+        if (e != hipSuccess) return from_hip(e, name);
+    }
+    return ok();
+}
+
+CPATTN_API cpattn_status_t cpattn_block_bwd(const void* q, const void* k, const void* v, const void* dout,
+                                            cpattn_dtype_t dtype, int32_t batch, int64_t seq_q, int64_t seq_kv,
+                                            int32_t heads_q, int32_t heads_kv, int32_t head_dim,
+                                            const int64_t* q_positions, const int64_t* kv_positions,
+                                            float scale, const float* lse, const float* delta, float* dq,
+                                            float* dk, float* dv, uint32_t flags, void* stream) {
+    const char* name = "block_bwd";
+    if (flags & ~(uint32_t)(CPATTN_BWD_WRITE_DQ | CPATTN_BWD_WRITE_DKV))
+        return fail(CPATTN_ERR_INVALID_ARG, "%s: unknown flags 0x%x", name, flags);
+    const bool wdq = (flags & CPATTN_BWD_WRITE_DQ) != 0, wdkv = (flags & CPATTN_BWD_WRITE_DKV) != 0;
+    bool empty = false;
+    const cpattn_status_t st =
+        block_bwd_check(name, q, k, v, dout, dtype, batch, seq_q, seq_kv, heads_q, heads_kv, head_dim,
+                        q_positions, kv_positions, scale, lse, delta, dq, dk, dv, wdq, wdkv, &empty);
+    if (st != CPATTN_OK) return st;
+    if (empty) return block_bwd_empty(name, batch, seq_q, seq_kv, heads_q, heads_kv, head_dim, dq, dk, dv, wdq, wdkv,
+                                      stream);
     cpattn::BlockBwdArgs a{q,  k,     v,     dout,   q_positions, kv_positions, lse,      delta, dq, dk,
                            dv, batch, seq_q, seq_kv, heads_q,     heads_kv,     head_dim, scale, wdq, wdkv};
     const hipError_t e = (dtype == CPATTN_BF16) ? cpattn::launch_block_bwd_bf16(a, (hipStream_t)stream)
                                                 : cpattn::launch_block_bwd_f32(a, (hipStream_t)stream);
     return from_hip(e, name);
+}
+
+CPATTN_API cpattn_status_t cpattn_ring_share_bwd(const void* q, const void* dout, const void* const* k_blocks,
+                                                 const void* const* v_blocks,
+                                                 const int64_t* const* kv_positions, const int64_t* seq_kv,
+                                                 int32_t n_blocks, cpattn_dtype_t dtype, int32_t batch,
+                                                 int64_t seq_q, int32_t heads_q, int32_t heads_kv,
+                                                 int32_t head_dim, const int64_t* q_positions, float scale,
+                                                 const float* lse, const float* delta, float* dq,
+                                                 float* const* dk_blocks, float* const* dv_blocks, void* stream) {
+    const char* name = "ring_share_bwd";
+    if (n_blocks <= 0 || n_blocks > cpattn::kMaxRingBlocks)
+        return fail(CPATTN_ERR_INVALID_ARG, "%s: n_blocks %d outside [1, %d]", name, n_blocks,
+                    cpattn::kMaxRingBlocks);
+    if (!k_blocks || !v_blocks || !kv_positions || !seq_kv || !dk_blocks || !dv_blocks)
+        return fail(CPATTN_ERR_INVALID_ARG, "%s: NULL block array", name);
+    // every block validated as a single-block call (dq written by the first, dk and dv by
+    // their own block) before anything is enqueued
+    bool any_pairs = false;
+    for (int32_t o = 0; o < n_blocks; ++o) {
+        bool empty = false;
+        const cpattn_status_t st = block_bwd_check(name, q, k_blocks[o], v_blocks[o], dout, dtype, batch, seq_q,
+                                                   seq_kv[o], heads_q, heads_kv, head_dim, q_positions,
+                                                   kv_positions[o], scale, lse, delta, dq, dk_blocks[o],
+                                                   dv_blocks[o], o == 0, true, &empty);
+        if (st != CPATTN_OK) return st;
+        any_pairs = any_pairs || !empty;
+    }
+    if (!any_pairs) {
+        // no pair in any block: dq and every block's dk, dv become zero
+        for (int32_t o = 0; o < n_blocks; ++o) {
+            const cpattn_status_t st = block_bwd_empty(name, batch, seq_q, seq_kv[o], heads_q, heads_kv, head_dim,
+                                                       dq, dk_blocks[o], dv_blocks[o], o == 0, true, stream);
+            if (st != CPATTN_OK) return st;
+        }
+        return ok();
+    }
+    if (dtype != CPATTN_BF16) {
+        // fp32: the per-step calls, the first writing dq and each block writing its dk, dv
+        for (int32_t o = 0; o < n_blocks; ++o) {
+            const cpattn_status_t st = cpattn_block_bwd(
+                q, k_blocks[o], v_blocks[o], dout, dtype, batch, seq_q, seq_kv[o], heads_q, heads_kv, head_dim,
+                q_positions, kv_positions[o], scale, lse, delta, dq, dk_blocks[o], dv_blocks[o],
+                CPATTN_BWD_WRITE_DKV | (o == 0 ? CPATTN_BWD_WRITE_DQ : 0u), stream);
+            if (st != CPATTN_OK) return st;
+        }
+        return ok();
+    }
+    // the dk/dv launch: (longest block's 128-key blocks) x (blocks) x (batch, kv head) workgroups
+    int64_t max_kb = 0;
+    for (int32_t o = 0; o < n_blocks; ++o) max_kb = std::max(max_kb, (seq_kv[o] + 127) / 128);
+    if (max_kb * n_blocks * batch * heads_kv > kMaxGrid)
+        return fail(CPATTN_ERR_UNSUPPORTED, "%s: launch grid too large", name);
+    cpattn::RingBwdBlock blocks[cpattn::kMaxRingBlocks];
+    for (int32_t o = 0; o < n_blocks; ++o)
+        blocks[o] = cpattn::RingBwdBlock{k_blocks[o], v_blocks[o], kv_positions[o], seq_kv[o], dk_blocks[o],
+                                         dv_blocks[o]};
+    const cpattn::BlockBwdArgs a{q,       nullptr, nullptr, dout,     q_positions, nullptr, lse,   delta,
+                                 dq,      nullptr, nullptr, batch,    seq_q,       0,       heads_q, heads_kv,
+                                 head_dim, scale,  true,    true};
+    return from_hip(cpattn::launch_ring_bwd_bf16(a, n_blocks, blocks, (hipStream_t)stream), name);
 }
 
 CPATTN_API cpattn_status_t cpattn_ring_share_fwd(const void* q, const void* const* k_blocks,

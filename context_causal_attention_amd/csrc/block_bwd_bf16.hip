@@ -54,6 +54,17 @@ constexpr int kNW = 4;                      // waves per block
 constexpr int kThreads = 64 * kNW;
 constexpr float kLog2e = 1.4426950408889634f;
 
+// One K/V block of a dk/dv launch: its keys, values, positions and gradient buffers.
+struct BwdKV {
+    const __bf16* k;
+    const __bf16* v;
+    const int64_t* kvpos;
+    float* dk;
+    float* dv;
+    int64_t seq_kv;
+    int64_t n_kb;  // key blocks of 128 keys
+};
+
 struct BwdParams {
     const __bf16* q;
     const __bf16* k;
@@ -87,6 +98,14 @@ struct BwdParams {
     int32_t kv_xcd_cols;
     int32_t write_dq;   // overwrite instead of adding
     int32_t write_dkv;
+    // dk/dv launch: the K/V blocks it covers (a single-block call fills kv[0] from k, v,
+    // kvpos, dk, dv); workgroups take key block kb of block o in the order (o, kb): the
+    // workgroups running at one time mostly share a block, so they stream the same query
+    // tiles through L2 (interleaving the blocks by key block lost 6% on the 256K share), and
+    // the launch has no gap between one block's last workgroups and the next block's
+    int32_t n_blk;
+    int64_t max_n_kb;
+    BwdKV kv[kMaxRingBlocks];
 };
 
 __device__ inline int wave_sum(int x) {
@@ -502,14 +521,23 @@ __global__ void __launch_bounds__(kThreadsKv, 1) block_bwd_dkdv_kernel(const Bwd
         col = (int)(blockIdx.x % p.kv_cols);
         kb_rank = blockIdx.x / p.kv_cols;
     }
-    const int64_t kblk = kb_rank;  // early keys (most queries) first
+    // the blocks one after another, each with its early keys (most queries) first (the grid
+    // stays below 2^31)
+    const int o = (int)((uint32_t)kb_rank / (uint32_t)p.max_n_kb);
+    const int64_t kblk = (int64_t)((uint32_t)kb_rank % (uint32_t)p.max_n_kb);
+    const BwdKV& blk = p.kv[o];
+    if (kblk >= blk.n_kb) return;  // a shorter block: nothing here (the whole workgroup)
+    const __bf16* const kbuf = blk.k;
+    const __bf16* const vbuf = blk.v;
+    const int64_t* const kvpos = blk.kvpos;
+    const int64_t seq_kv = blk.seq_kv;
     const int kvh = col % p.heads_kv;
     const int64_t b = col / p.heads_kv;
 
     const int64_t k0 = kblk * (32 * kNW);
-    const int64_t k_last = (k0 + 32 * kNW < p.seq_kv ? k0 + 32 * kNW : p.seq_kv) - 1;
-    const int64_t kmin = p.kvpos[k0];
-    const int64_t kmax = p.kvpos[k_last];
+    const int64_t k_last = (k0 + 32 * kNW < seq_kv ? k0 + 32 * kNW : seq_kv) - 1;
+    const int64_t kmin = kvpos[k0];
+    const int64_t kmax = kvpos[k_last];
 
     // query tiles that see some key of the block (a suffix, from qt_lo) and tiles whose every
     // query sees every key of the block (a shorter suffix, from qt_full)
@@ -541,23 +569,23 @@ __global__ void __launch_bounds__(kThreadsKv, 1) block_bwd_dkdv_kernel(const Bwd
 
     // this lane's key row: k and v as B operands
     const int64_t key = k0 + kg * 32 + l32;
-    const bool kvalid = key < p.seq_kv;
-    const int64_t krow = (b * p.seq_kv + (kvalid ? key : 0)) * p.heads_kv + kvh;
+    const bool kvalid = key < seq_kv;
+    const int64_t krow = (b * seq_kv + (kvalid ? key : 0)) * p.heads_kv + kvh;
     bf16x8 kreg[kD / 16];
 #pragma unroll
-    for (int ks = 0; ks < kD / 16; ++ks) kreg[ks] = load_row16(p.k + krow * kD + 16 * ks + 8 * half, kvalid);
+    for (int ks = 0; ks < kD / 16; ++ks) kreg[ks] = load_row16(kbuf + krow * kD + 16 * ks + 8 * half, kvalid);
     // V rows go to LDS once (the first-half waves write their key group's rows) and are read
     // as the dP operand with the same swizzled row offsets as the Q and dO tiles
     LDS_AS char* vl = (LDS_AS char*)lds_v + (kg + 1) * 32 * kRowBytes;
     if (qhalf == 0) {
 #pragma unroll
         for (int ks = 0; ks < kD / 16; ++ks)
-            *(LDS_AS bf16x8*)(vl + BG::row_off(lane, ks)) = load_row16(p.v + krow * kD + 16 * ks + 8 * half, kvalid);
+            *(LDS_AS bf16x8*)(vl + BG::row_off(lane, ks)) = load_row16(vbuf + krow * kD + 16 * ks + 8 * half, kvalid);
     }
     // first query row that sees this key (rows before it are masked), when some tile is partial
     int64_t first = 0;
     if (qt_lo < qt_full) {
-        const int64_t kp = kvalid ? p.kvpos[key] : INT64_MAX;
+        const int64_t kp = kvalid ? kvpos[key] : INT64_MAX;
         int64_t lo = (int64_t)qt_lo * kTile;
         int64_t hi = (int64_t)qt_full * kTile < p.seq_q ? (int64_t)qt_full * kTile : p.seq_q;
         while (lo < hi) {
@@ -768,8 +796,8 @@ __global__ void __launch_bounds__(kThreadsKv, 1) block_bwd_dkdv_kernel(const Bwd
     }
     // dk += scale * dK, dv += dV; entry v of block db is dimension 32*db + 8*(v/4) + 4*half + v%4
     if (!kvalid || qhalf != 0) return;
-    float* krow_k = p.dk + krow * kD;
-    float* krow_v = p.dv + krow * kD;
+    float* krow_k = blk.dk + krow * kD;
+    float* krow_v = blk.dv + krow * kD;
 #pragma unroll
     for (int db = 0; db < kD / 32; ++db)
 #pragma unroll
@@ -792,7 +820,7 @@ __global__ void __launch_bounds__(kThreadsKv, 1) block_bwd_dkdv_kernel(const Bwd
 }
 
 template <int D>
-hipError_t launch_head_dim(const BwdParams& p, hipStream_t stream) {
+hipError_t launch_dq(const BwdParams& p, hipStream_t stream) {
     // launches of fewer than two blocks per CU split each tile's keys over two wave groups
     if (p.n_qt * p.n_cols < 512)
         hipLaunchKernelGGL((block_bwd_dq_kernel<D, 2>), dim3((unsigned)(p.n_qt * p.n_cols)), dim3(2 * kThreads), 0,
@@ -800,15 +828,18 @@ hipError_t launch_head_dim(const BwdParams& p, hipStream_t stream) {
     else
         hipLaunchKernelGGL((block_bwd_dq_kernel<D, 1>), dim3((unsigned)(p.n_qt * p.n_cols)), dim3(kThreads), 0,
                            stream, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(block_bwd_dkdv_kernel<D>, dim3((unsigned)(p.n_kb * p.kv_cols)), dim3(kThreadsKv), 0, stream, p);
     return hipGetLastError();
 }
 
-}  // namespace
+template <int D>
+hipError_t launch_dkdv(const BwdParams& p, hipStream_t stream) {
+    hipLaunchKernelGGL(block_bwd_dkdv_kernel<D>, dim3((unsigned)(p.max_n_kb * p.n_blk * p.kv_cols)),
+                       dim3(kThreadsKv), 0, stream, p);
+    return hipGetLastError();
+}
 
-hipError_t launch_block_bwd_bf16(const BlockBwdArgs& a, hipStream_t stream) {
+// The parameters of one block's call (dq and dk/dv of that block).
+BwdParams block_params(const BlockBwdArgs& a) {
     BwdParams p;
     p.q = (const __bf16*)a.q;
     p.k = (const __bf16*)a.k;
@@ -840,7 +871,53 @@ hipError_t launch_block_bwd_bf16(const BlockBwdArgs& a, hipStream_t stream) {
     p.kv_xcd_cols = (p.kv_cols % 8 == 0) ? p.kv_cols / 8 : 0;
     p.write_dq = a.write_dq ? 1 : 0;
     p.write_dkv = a.write_dkv ? 1 : 0;
-    return a.head_dim == 64 ? launch_head_dim<64>(p, stream) : launch_head_dim<128>(p, stream);
+    p.n_blk = 1;
+    p.max_n_kb = p.n_kb;
+    p.kv[0] = BwdKV{p.k, p.v, p.kvpos, p.dk, p.dv, p.seq_kv, p.n_kb};
+    return p;
+}
+
+}  // namespace
+
+hipError_t launch_block_bwd_bf16(const BlockBwdArgs& a, hipStream_t stream) {
+    const BwdParams p = block_params(a);
+    hipError_t e = a.head_dim == 64 ? launch_dq<64>(p, stream) : launch_dq<128>(p, stream);
+    if (e != hipSuccess) return e;
+    return a.head_dim == 64 ? launch_dkdv<64>(p, stream) : launch_dkdv<128>(p, stream);
+}
+
+hipError_t launch_ring_bwd_bf16(const BlockBwdArgs& a, int32_t n_blk, const RingBwdBlock* blocks,
+                                hipStream_t stream) {
+    // dq: the blocks one launch after another, the first that has keys writing, the others
+    // adding (as the per-step calls do); blocks without keys add nothing
+    bool first = true;
+    for (int32_t o = 0; o < n_blk; ++o) {
+        if (blocks[o].seq_kv == 0) continue;
+        BlockBwdArgs b = a;
+        b.k = blocks[o].k;
+        b.v = blocks[o].v;
+        b.kv_pos = blocks[o].pos;
+        b.seq_kv = blocks[o].seq_kv;
+        b.write_dq = first;
+        first = false;
+        const BwdParams p = block_params(b);
+        const hipError_t e = a.head_dim == 64 ? launch_dq<64>(p, stream) : launch_dq<128>(p, stream);
+        if (e != hipSuccess) return e;
+    }
+    // dk, dv: every block's key blocks in one launch (each written)
+    BwdParams p = block_params(a);
+    p.write_dkv = 1;
+    p.n_blk = 0;
+    p.max_n_kb = 0;
+    for (int32_t o = 0; o < n_blk; ++o) {
+        if (blocks[o].seq_kv == 0) continue;
+        const int64_t n_kb = (blocks[o].seq_kv + 32 * kNW - 1) / (32 * kNW);
+        p.kv[p.n_blk++] = BwdKV{(const __bf16*)blocks[o].k, (const __bf16*)blocks[o].v, blocks[o].pos,
+                                blocks[o].dk, blocks[o].dv, blocks[o].seq_kv, n_kb};
+        if (n_kb > p.max_n_kb) p.max_n_kb = n_kb;
+    }
+    if (p.n_blk == 0) return hipSuccess;
+    return a.head_dim == 64 ? launch_dkdv<64>(p, stream) : launch_dkdv<128>(p, stream);
 }
 
 }  // namespace cpattn

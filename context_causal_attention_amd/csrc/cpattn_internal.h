@@ -100,6 +100,19 @@ hipError_t launch_attn_bwd_delta(const float* out, const void* dout, bool bf16, 
 // One block's backward, accumulated into dq, dk, dv (fp32 and bf16 paths).
 hipError_t launch_block_bwd_f32(const BlockBwdArgs& a, hipStream_t stream);
 hipError_t launch_block_bwd_bf16(const BlockBwdArgs& a, hipStream_t stream);
+// A ring share's backward over n_blk blocks (bf16): dq written with the sum over the blocks,
+// each block's dk and dv written to its own buffers.  a supplies the query side (q, dout,
+// q_pos, lse, delta, dq, shapes, scale); its k, v, kv_pos, seq_kv, dk, dv are not used.
+struct RingBwdBlock {
+    const void* k;
+    const void* v;
+    const int64_t* pos;
+    int64_t seq_kv;
+    float* dk;
+    float* dv;
+};
+hipError_t launch_ring_bwd_bf16(const BlockBwdArgs& a, int32_t n_blk, const RingBwdBlock* blocks,
+                                hipStream_t stream);
 // n floats of p set to 0 (an accumulator that no block writes)
 hipError_t launch_zero_fill(float* p, int64_t n, hipStream_t stream);
 

@@ -303,6 +303,34 @@ cpattn_status_t cpattn_block_bwd(const void* q, const void* k, const void* v, co
                                  uint32_t flags, void* stream);
 
 /*
+ * cpattn_ring_share_bwd -- a rank's whole backward share: the gradients from the queries
+ * against C K/V blocks, as [CP] "Peer-to-peer" / "Backward" computes them step by step
+ * (cpattn_block_bwd once per block, dq summed locally over the steps, each block's dk and dv
+ * going to the buffers that travel with it).  The same arithmetic as those calls with
+ * CPATTN_BWD_WRITE_DKV on every block and CPATTN_BWD_WRITE_DQ on the first; for bf16 the
+ * dk and dv of all blocks come from one launch, so that the blocks' key ranges fill the chip
+ * together (one launch per block leaves it partly empty wherever half a block's keys are
+ * hidden from every query, as in the zigzag ring steps).
+ *
+ *   q, dout, q_positions, scale, lse, delta   as for cpattn_block_bwd
+ *   k_blocks, v_blocks, kv_positions, seq_kv, n_blocks   as for cpattn_ring_share_fwd
+ *   dq          out fp32 [batch][seq_q][heads_q][head_dim]: the sum of the blocks' parts
+ *   dk_blocks, dv_blocks   host arrays of n_blocks DEVICE pointers, block o's dk and dv,
+ *               out fp32 [batch][seq_kv[o]][heads_kv][head_dim] (written)
+ * dk, dv of every block and dq are the same bits as the per-block calls give.  Every block is
+ * validated before anything is enqueued.
+ * Errors: as for cpattn_block_bwd on each block, and INVALID_ARG for n_blocks outside [1, 16]
+ * or NULL arrays.
+ */
+cpattn_status_t cpattn_ring_share_bwd(const void* q, const void* dout, const void* const* k_blocks,
+                                      const void* const* v_blocks, const int64_t* const* kv_positions,
+                                      const int64_t* seq_kv, int32_t n_blocks, cpattn_dtype_t dtype,
+                                      int32_t batch, int64_t seq_q, int32_t heads_q, int32_t heads_kv,
+                                      int32_t head_dim, const int64_t* q_positions, float scale,
+                                      const float* lse, const float* delta, float* dq,
+                                      float* const* dk_blocks, float* const* dv_blocks, void* stream);
+
+/*
  * cpattn_reorder_gathered -- chunk reorder between the all-gather's rank order and the
  * global sequence order.  [CP] "All-gather": the gather concatenates the ranks' zigzag
  * shards in rank order (at C=4: chunks 0,7,1,6,2,5,3,4), and K/V must be put back in

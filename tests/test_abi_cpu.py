@@ -230,6 +230,46 @@ def test_block_bwd_validation(lib):
     assert _bb(lib, seq_q=0, flags=2, dv=NULL) == INVALID
 
 
+def _rb(lib, n=4, seqs=None, ks=None, vs=None, ps=None, dks=None, dvs=None, arrays=True, **kw):
+    seqs = seqs if seqs is not None else [64] * n
+    ks, vs, ps, dks, dvs = ([0x1000] * n if x is None else x for x in (ks, vs, ps, dks, dvs))
+    a = dict(q=FAKE, dout=FAKE, dtype=1, batch=1, seq_q=64, hq=4, hkv=2, d=128, qpos=FAKE, scale=0.1, lse=FAKE,
+             delta=FAKE, dq=FAKE, n_blocks=n)
+    a.update(kw)
+    arr = ctypes.c_void_p * max(n, 1)
+    blk = (lambda x: arr(*x)) if arrays else (lambda x: None)
+    return lib.cpattn_ring_share_bwd(a["q"], a["dout"], blk(ks), blk(vs), blk(ps), (ctypes.c_int64 * max(n, 1))(*seqs),
+                                     a["n_blocks"], a["dtype"], a["batch"], a["seq_q"], a["hq"], a["hkv"], a["d"],
+                                     a["qpos"], a["scale"], a["lse"], a["delta"], a["dq"], blk(dks), blk(dvs), NULL)
+
+
+def test_ring_share_bwd_validation(lib):
+    assert _rb(lib, n_blocks=0) == INVALID
+    assert _rb(lib, n=17) == INVALID and "n_blocks" in _err(lib)
+    assert _rb(lib, arrays=False) == INVALID and "NULL block array" in _err(lib)
+    assert _rb(lib, seqs=[64, -1, 64, 64]) == INVALID
+    assert _rb(lib, dtype=7) == INVALID
+    assert _rb(lib, batch=0) == INVALID
+    assert _rb(lib, scale=float("nan")) == INVALID
+    assert _rb(lib, hq=6, hkv=4) == SHAPE
+    assert _rb(lib, d=96) == UNSUPPORTED
+    assert _rb(lib, hq=(1 << 17) + 2, hkv=2) == UNSUPPORTED and "2^24" in _err(lib)
+    for name in ("q", "dout", "qpos", "lse", "delta", "dq"):
+        assert _rb(lib, **{name: NULL}) == INVALID, name
+    # each block as a single-block call: its pointers, their alignment
+    assert _rb(lib, ks=[0x1000, 0, 0x1000, 0x1000]) == INVALID
+    assert _rb(lib, ps=[0x1000, 0x1000, 0, 0x1000]) == INVALID
+    assert _rb(lib, dks=[0x1000, 0x1000, 0x1000, 0]) == INVALID
+    assert _rb(lib, dvs=[0x1000, 0x1004, 0x1000, 0x1000]) == UNSUPPORTED and "aligned" in _err(lib)
+    # a block without keys may hold NULL pointers; no pair anywhere and nothing to overwrite: a no-op
+    z = [0] * 4
+    assert _rb(lib, seq_q=0, seqs=z, ks=z, vs=z, ps=z, dks=z, dvs=z, q=NULL, dout=NULL, qpos=NULL, dq=NULL) == OK
+    # every block is checked before anything is enqueued, for either dtype (without a GPU, a
+    # launch would have returned CPATTN_ERR_HIP instead)
+    assert _rb(lib, dtype=0, ps=[0x1000, 0x1000, 0x1000, 0]) == INVALID
+    assert _rb(lib, dtype=1, dvs=[0x1000, 0x1000, 0x1000, 0]) == INVALID
+
+
 def _rs(lib, n=4, seqs=None, ks=None, vs=None, ps=None, **kw):
     seqs = seqs if seqs is not None else [64] * n
     ks = ks if ks is not None else [0x1000] * n

@@ -254,6 +254,66 @@ def _ring_bwd_check(w, rows_per_chunk, key_samples, exact_forward):
         print(f"{w.name}: owner {o} dk, dv checked on {len(krows)} keys", flush=True)
 
 
+@pytest.mark.parametrize("dtype,C,t,Hq,Hkv,D,B,rank", [
+    ("bf16", 4, 100, 4, 2, 128, 1, 1),   # ragged tiles, GQA
+    ("bf16", 3, 70, 8, 8, 64, 2, 2),     # head dim 64, batch 2, the last rank
+    ("bf16", 8, 256, 32, 8, 128, 1, 3),  # whole tiles, the long share's head layout
+    ("fp32", 2, 33, 4, 2, 64, 1, 0),
+])
+def test_ring_share_bwd_single_equals_steps(dtype, C, t, Hq, Hkv, D, B, rank):
+    """The share's backward in one call (cpattn_ring_share_bwd: dq per step, dk and dv of all
+    blocks in one launch) gives the same bits as one cpattn_block_bwd per ring step."""
+    S = 2 * C * t
+    pos = [cp.zigzag_index(S, C, o, device=DEV) for o in range(C)]
+    ks = [_rand(300 + o, (B, 2 * t, Hkv, D), dtype).to(DEV) for o in range(C)]
+    vs = [_rand(400 + o, (B, 2 * t, Hkv, D), dtype).to(DEV) for o in range(C)]
+    q, g = _rand(1, (B, 2 * t, Hq, D), dtype).to(DEV), _rand(2, (B, 2 * t, Hq, D), dtype).to(DEV)
+    scale = 1 / math.sqrt(D)
+    out, lse = cp.ring_share_fwd(q, ks, vs, pos, rank, scale)
+    res = {}
+    for mode in ("single", "steps"):
+        dq = torch.full((B, 2 * t, Hq, D), 7.0, device=DEV)  # every buffer is overwritten
+        dks = [torch.full(k.shape, 7.0, device=DEV) for k in ks]
+        dvs = [torch.full(v.shape, 7.0, device=DEV) for v in vs]
+        res[mode] = cp.ring_share_bwd(q, ks, vs, pos, rank, scale, out, lse, g, dq=dq, dk_blocks=dks,
+                                      dv_blocks=dvs, mode=mode)
+    torch.cuda.synchronize()
+    a, b = res["single"], res["steps"]
+    assert torch.equal(a[0], b[0])
+    for o in range(C):
+        assert torch.equal(a[1][o], b[1][o]) and torch.equal(a[2][o], b[2][o]), o
+
+
+def test_ring_blocks_bwd_unequal_and_empty_blocks():
+    """Blocks of different lengths (the dk/dv launch is sized by the longest; shorter blocks'
+    missing key blocks do nothing) and a block without keys, against per-block calls."""
+    B, Sq, Hq, Hkv, D = 1, 300, 4, 2, 128
+    lens = [500, 0, 130, 257]
+    qpos = torch.arange(600, 600 + Sq, device=DEV)
+    kpos = [torch.sort(torch.randperm(900, generator=torch.Generator().manual_seed(o))[:n]).values.to(DEV)
+            for o, n in enumerate(lens)]
+    ks = [_rand(500 + o, (B, n, Hkv, D), "bf16").to(DEV) for o, n in enumerate(lens)]
+    vs = [_rand(600 + o, (B, n, Hkv, D), "bf16").to(DEV) for o, n in enumerate(lens)]
+    q, g = _rand(3, (B, Sq, Hq, D), "bf16").to(DEV), _rand(4, (B, Sq, Hq, D), "bf16").to(DEV)
+    scale = 1 / math.sqrt(D)
+    out, lse = cp.ring_blocks_fwd(q, ks, vs, kpos, qpos, scale)
+    delta = cp.attn_bwd_delta(out, g)
+    dq = torch.full((B, Sq, Hq, D), 7.0, device=DEV)
+    dks = [torch.full(k.shape, 7.0, device=DEV) for k in ks]
+    dvs = [torch.full(v.shape, 7.0, device=DEV) for v in vs]
+    cp.ring_blocks_bwd(q, g, ks, vs, kpos, qpos, scale, lse, delta, dq, dks, dvs)
+    rq = torch.empty_like(dq)
+    rk = [torch.empty_like(x) for x in dks]
+    rv = [torch.empty_like(x) for x in dvs]
+    for o in range(len(lens)):
+        cp.block_bwd(q, ks[o], vs[o], g, qpos, kpos[o], scale, lse, delta, rq, rk[o], rv[o],
+                     cp.BWD_WRITE_DKV | (cp.BWD_WRITE_DQ if o == 0 else 0))
+    torch.cuda.synchronize()
+    assert torch.equal(dq, rq)
+    for o in range(len(lens)):
+        assert torch.equal(dks[o], rk[o]) and torch.equal(dvs[o], rv[o]), o
+
+
 def test_ring_share_bwd_8k():
     _ring_bwd_check(WORKLOADS["rank_share_8k"], rows_per_chunk=12, key_samples=12, exact_forward=True)
 
