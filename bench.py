@@ -792,8 +792,8 @@ def main(argv=None) -> int:
 # same group as the library's Ulysses share runs it, the exchanges folded into the attention's
 # row addressing; the long-context ring share in its per-step form, one attention launch per
 # ring step into a tile and the merge kernel after each ("On Context Parallelism",
-# Peer-to-peer / Forward); and that share's backward, delta once and one dq and one dk/dv
-# launch per ring step ("On Context Parallelism", Peer-to-peer / Backward).
+# Peer-to-peer / Forward); and that share's backward, delta once, one dq launch per ring step
+# and one dk/dv launch over all the blocks ("On Context Parallelism", Peer-to-peer / Backward).
 EXTRAS = [("ulysses_gqa_128k", "single"), ("ulysses_gqa_128k", "fused"), ("ring_share_256k", "unfused"),
           ("ring_share_256k", "bwd")]
 
