@@ -284,11 +284,12 @@ def test_ring_share_bwd_single_equals_steps(dtype, C, t, Hq, Hkv, D, B, rank):
         assert torch.equal(a[1][o], b[1][o]) and torch.equal(a[2][o], b[2][o]), o
 
 
-def test_ring_blocks_bwd_unequal_and_empty_blocks():
+@pytest.mark.parametrize("lens", [[500, 0, 130, 257], [64 + 37 * o for o in range(16)]])
+def test_ring_blocks_bwd_unequal_and_empty_blocks(lens):
     """Blocks of different lengths (the dk/dv launch is sized by the longest; shorter blocks'
-    missing key blocks do nothing) and a block without keys, against per-block calls."""
+    missing key blocks do nothing), a block without keys, and the most blocks one call takes
+    (16), against per-block calls."""
     B, Sq, Hq, Hkv, D = 1, 300, 4, 2, 128
-    lens = [500, 0, 130, 257]
     qpos = torch.arange(600, 600 + Sq, device=DEV)
     kpos = [torch.sort(torch.randperm(900, generator=torch.Generator().manual_seed(o))[:n]).values.to(DEV)
             for o, n in enumerate(lens)]
