@@ -31,8 +31,11 @@
 // At the end the second-half waves hand their partial dK, dV to the first-half waves through
 // LDS, which add them and write the result.
 // The causal structure is used as in the forward: tiles entirely hidden are skipped, tiles
-// entirely visible need no mask, and partly visible tiles compare row indices with a count
-// found once by binary search over the positions.
+// entirely visible need no mask, and on partly visible tiles the packed bf16 weights of hidden
+// pairs are cleared, by comparing row indices with a count found once by binary search over
+// the positions.
+// cpattn_ring_share_bwd runs the dq kernel once per K/V block and the dk/dv kernel once over
+// all the blocks (each workgroup one block's 128 keys of one K/V head).
 #include "cpattn_internal.h"
 
 #include <math.h>
