@@ -51,9 +51,15 @@
 // are a shorter prefix; only the tiles in between are masked element by element, against
 // each row's count of visible keys (found once by binary search over the key positions).
 // Rows with no visible key end with out = 0 and lse = -inf.
+//
+// Block order: heaviest query tiles first, a K/V head's columns on one XCD.  Launches of at
+// least four rounds of blocks take their tiles from queues at run time (an atomic add per
+// block; one queue per XCD, taking the others' last tiles once its own run out), since the
+// XCDs hold different clocks under load and equal shares would end at different times.
 #include "cpattn_internal.h"
 #include "merge_math.h"
 
+#include <atomic>
 #include <math.h>
 
 namespace cpattn {
@@ -73,6 +79,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.0f;       // raise the running max only past this margin (log2)
 constexpr float kLazyWeight = 256.0f;  // 2^kLazy
 constexpr int kMaxBlocks = kMaxRingBlocks;  // K/V blocks of one launch
+constexpr int64_t kQueueMinBlocks = 1024;    // launches with at least 4 rounds of blocks use the queues
 constexpr int kVisKeys = 256;               // key positions a wave searches in LDS
 
 // One K/V block: keys [B][seq][heads_kv][D] and their positions.
@@ -105,7 +112,22 @@ struct Params {
     int64_t kv_rs;     // row are contiguous: dense rows have heads * D)
     int64_t out_rs;
     KVBlock blk[kMaxBlocks];
+    // work taken from queues at run time (per_q > 0) instead of by block index: n_queues
+    // queues (8: one per XCD, holding its columns' tiles; 1: all tiles) of per_q tiles each,
+    // counted in counter slot `slot`
+    int32_t n_queues;
+    int32_t slot;
+    int64_t per_q;
 };
+
+// Work counters of the launches that take their tiles from queues: a slot per call, taken in
+// turn (so calls in flight on different streams use different slots), 16 counters per slot
+// (one per queue), set to zero by a one-workgroup kernel on the call's stream before the
+// attention launch.  Device code reaches the array by name; host code never uses it.
+constexpr int kCtrSlots = 256;
+__device__ int g_fwd_ctr[kCtrSlots * 16];
+
+__global__ void fwd_ctr_reset_kernel(int slot) { g_fwd_ctr[slot * 16 + threadIdx.x] = 0; }
 
 __device__ inline int wave_sum(int x) {
 #pragma unroll
@@ -200,7 +222,41 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
     // ---- which (b, kv head, head group, query tile) this block owns; heavy tiles first
     int col;
     int64_t qt_rank;
-    if (p.xcd_cols > 0) {
+    if (p.per_q > 0) {
+        // From the queues: the hardware deals consecutive blocks to the 8 XCDs in turn, and
+        // the XCDs run at different clocks under load, so equal shares of blocks end at
+        // different times.  A block takes the next tile of its XCD's queue (its columns, heavy
+        // tiles first), or, once that is empty, of the next queue that is not; a block that
+        // finds every queue empty has nothing to do.  Each tile is computed by exactly one
+        // block, with the same code wherever it runs.
+        __shared__ int claim[2];
+        if (threadIdx.x == 0) {
+            const int home = p.n_queues > 1 ? (int)(blockIdx.x & 7) : 0;
+            int q = -1, it = 0;
+            for (int y = 0; y < p.n_queues; ++y) {
+                const int qq = (home + y) % p.n_queues;
+                const int i = atomicAdd(&g_fwd_ctr[p.slot * 16 + qq], 1);
+                if (i < p.per_q) {
+                    q = qq;
+                    it = i;
+                    break;
+                }
+            }
+            claim[0] = q;
+            claim[1] = it;
+        }
+        __syncthreads();
+        const int q = claim[0];
+        if (q < 0) return;  // the whole block
+        const int64_t it = claim[1];
+        if (p.n_queues > 1) {
+            qt_rank = it / p.xcd_cols;
+            col = q + 8 * (int)(it % p.xcd_cols);
+        } else {
+            col = (int)(it % p.n_cols);
+            qt_rank = it / p.n_cols;
+        }
+    } else if (p.xcd_cols > 0) {
         // consecutive blocks are dealt round-robin to the 8 XCDs: keep one XCD on the same
         // columns (same K/V head) so its L2 serves all of them
         const int x = blockIdx.x & 7;
@@ -719,12 +775,36 @@ __global__ void __launch_bounds__(64 * NW, 1) block_fwd_bf16_kernel(const Params
     }
 }
 
+std::atomic<uint32_t> g_next_slot{0};
+
 template <int D, int NW, int NB, int KBP, int KS>
 hipError_t launch_variant(Params p, int64_t seq_q, hipStream_t stream) {
     p.pq = 32 * (NW / KS) * NB / p.G;
     p.n_qt = (seq_q + p.pq - 1) / p.pq;
     const int64_t blocks = p.n_qt * p.n_cols;
-    hipLaunchKernelGGL((block_fwd_bf16_kernel<D, NW, NB, KBP, KS>), dim3((unsigned)blocks), dim3(64 * NW), 0, stream, p);
+    int64_t grid = blocks;
+    p.n_queues = 1;
+    p.slot = 0;
+    p.per_q = 0;
+    // Launches of at least four rounds of blocks take their tiles from queues, with a quarter
+    // more blocks (and at least 64 more per XCD) than tiles, so that the XCDs that finish
+    // their own queue early have blocks left to take the others' last tiles with.
+    if (blocks >= kQueueMinBlocks) {
+        p.n_queues = p.xcd_cols > 0 ? 8 : 1;
+        p.per_q = blocks / p.n_queues;  // exact: with 8 queues, n_cols = 8 * xcd_cols
+        const int64_t extra = p.per_q / 4 + 64;
+        grid = p.n_queues * p.per_q + 8 * extra;
+        if (grid > INT32_MAX) {
+            grid = blocks;
+            p.per_q = 0;
+            p.n_queues = 1;
+        }
+    }
+    if (p.per_q > 0) {
+        p.slot = (int32_t)(g_next_slot.fetch_add(1, std::memory_order_relaxed) % kCtrSlots);
+        hipLaunchKernelGGL(fwd_ctr_reset_kernel, dim3(1), dim3(16), 0, stream, p.slot);
+    }
+    hipLaunchKernelGGL((block_fwd_bf16_kernel<D, NW, NB, KBP, KS>), dim3((unsigned)grid), dim3(64 * NW), 0, stream, p);
     return hipGetLastError();
 }
 
