@@ -36,8 +36,12 @@
 // the positions.
 // cpattn_ring_share_bwd runs the dq kernel once per K/V block and the dk/dv kernel once over
 // all the blocks (each workgroup one block's 128 keys of one K/V head).
+// Launches of at least eight rounds of workgroups take their items from queues at run time
+// (one per XCD, taking the others' last items once its own run out), as the forward does:
+// the XCDs hold different clocks under load, and equal shares would end at different times.
 #include "cpattn_internal.h"
 
+#include <atomic>
 #include <math.h>
 
 namespace cpattn {
@@ -109,7 +113,50 @@ struct BwdParams {
     int32_t n_blk;
     int64_t max_n_kb;
     BwdKV kv[kMaxRingBlocks];
+    // work taken from queues at run time (per_q > 0; set by each launch for its own grid):
+    // n_queues queues (8: one per XCD, holding its columns' work; 1: all of it) of per_q
+    // items each, counted in counter slot `slot`
+    int32_t n_queues;
+    int32_t slot;
+    int64_t per_q;
 };
+
+// Work counters of the launches that take their items from queues: a slot per launch, taken
+// in turn, 16 counters per slot, zeroed by a one-workgroup kernel on the launch's stream.
+// Device code reaches the array by name; host code never uses it.
+constexpr int kCtrSlots = 256;
+__device__ int g_bwd_ctr[kCtrSlots * 16];
+
+__global__ void bwd_ctr_reset_kernel(int slot) { g_bwd_ctr[slot * 16 + threadIdx.x] = 0; }
+
+// The item a workgroup works on when its launch uses queues: the next one of its XCD's queue
+// (the hardware deals consecutive workgroups to the 8 XCDs in turn, and the XCDs hold
+// different clocks under load, so equal shares would end at different times), or, once that
+// queue is empty, of the next queue that is not.  Returns false when every queue is empty (the
+// whole workgroup then has nothing to do).  Each item is done by exactly one workgroup, with
+// the same code wherever it runs.
+__device__ inline bool claim_item(const BwdParams& p, int& queue, int64_t& item) {
+    __shared__ int claim[2];
+    if (threadIdx.x == 0) {
+        const int home = p.n_queues > 1 ? (int)(blockIdx.x & 7) : 0;
+        int q = -1, it = 0;
+        for (int y = 0; y < p.n_queues; ++y) {
+            const int qq = (home + y) % p.n_queues;
+            const int i = atomicAdd(&g_bwd_ctr[p.slot * 16 + qq], 1);
+            if (i < p.per_q) {
+                q = qq;
+                it = i;
+                break;
+            }
+        }
+        claim[0] = q;
+        claim[1] = it;
+    }
+    __syncthreads();
+    queue = claim[0];
+    item = claim[1];
+    return queue >= 0;
+}
 
 __device__ inline int wave_sum(int x) {
 #pragma unroll
@@ -252,7 +299,18 @@ __global__ void __launch_bounds__(64 * kNW * KS, 1) block_bwd_dq_kernel(const Bw
 
     int col;
     int64_t qt_rank;
-    if (p.xcd_cols > 0) {
+    if (p.per_q > 0) {
+        int q;
+        int64_t it;
+        if (!claim_item(p, q, it)) return;
+        if (p.n_queues > 1) {
+            qt_rank = it / p.xcd_cols;
+            col = q + 8 * (int)(it % p.xcd_cols);
+        } else {
+            col = (int)(it % p.n_cols);
+            qt_rank = it / p.n_cols;
+        }
+    } else if (p.xcd_cols > 0) {
         const int x = blockIdx.x & 7;
         const int64_t kk = blockIdx.x >> 3;
         qt_rank = kk / p.xcd_cols;
@@ -515,7 +573,18 @@ __global__ void __launch_bounds__(kThreadsKv, 1) block_bwd_dkdv_kernel(const Bwd
 
     int col;
     int64_t kb_rank;
-    if (p.kv_xcd_cols > 0) {
+    if (p.per_q > 0) {
+        int q;
+        int64_t it;
+        if (!claim_item(p, q, it)) return;
+        if (p.n_queues > 1) {
+            kb_rank = it / p.kv_xcd_cols;
+            col = q + 8 * (int)(it % p.kv_xcd_cols);
+        } else {
+            col = (int)(it % p.kv_cols);
+            kb_rank = it / p.kv_cols;
+        }
+    } else if (p.kv_xcd_cols > 0) {
         const int x = blockIdx.x & 7;
         const int64_t kk = blockIdx.x >> 3;
         kb_rank = kk / p.kv_xcd_cols;
@@ -822,22 +891,50 @@ __global__ void __launch_bounds__(kThreadsKv, 1) block_bwd_dkdv_kernel(const Bwd
         }
 }
 
+std::atomic<uint32_t> g_next_slot{0};
+
+// A launch of at least `min_items` workgroups (eight rounds of the chip) takes its work from
+// queues: one per XCD when the columns divide by 8 (xcd_cols > 0), else one, and a grid of a
+// quarter more workgroups than items (at least 64 more per XCD), so that the XCDs that finish
+// their own queue early have workgroups left to take the others' last items.  Returns the grid.
+int64_t use_queues(BwdParams& p, int64_t items, int64_t xcd_cols, int64_t min_items, hipStream_t stream) {
+    p.n_queues = 1;
+    p.slot = 0;
+    p.per_q = 0;
+    if (items < min_items) return items;
+    const int nq = xcd_cols > 0 ? 8 : 1;
+    const int64_t per_q = items / nq;  // exact: with 8 queues, the columns are 8 * xcd_cols
+    const int64_t grid = nq * per_q + 8 * (per_q / 4 + 64);
+    if (grid > INT32_MAX) return items;
+    p.n_queues = nq;
+    p.per_q = per_q;
+    p.slot = (int32_t)(g_next_slot.fetch_add(1, std::memory_order_relaxed) % kCtrSlots);
+    hipLaunchKernelGGL(bwd_ctr_reset_kernel, dim3(1), dim3(16), 0, stream, p.slot);
+    return grid;
+}
+
 template <int D>
-hipError_t launch_dq(const BwdParams& p, hipStream_t stream) {
+hipError_t launch_dq(BwdParams p, hipStream_t stream) {
+    const int64_t items = p.n_qt * p.n_cols;
     // launches of fewer than two blocks per CU split each tile's keys over two wave groups
-    if (p.n_qt * p.n_cols < 512)
-        hipLaunchKernelGGL((block_bwd_dq_kernel<D, 2>), dim3((unsigned)(p.n_qt * p.n_cols)), dim3(2 * kThreads), 0,
-                           stream, p);
-    else
-        hipLaunchKernelGGL((block_bwd_dq_kernel<D, 1>), dim3((unsigned)(p.n_qt * p.n_cols)), dim3(kThreads), 0,
-                           stream, p);
+    if (items < 512) {
+        p.per_q = 0;
+        hipLaunchKernelGGL((block_bwd_dq_kernel<D, 2>), dim3((unsigned)items), dim3(2 * kThreads), 0, stream, p);
+    } else {
+        // two 4-wave blocks per CU: eight rounds are 4096 blocks
+        const int64_t grid = use_queues(p, items, p.xcd_cols, 4096, stream);
+        hipLaunchKernelGGL((block_bwd_dq_kernel<D, 1>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+    }
     return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_dkdv(const BwdParams& p, hipStream_t stream) {
-    hipLaunchKernelGGL(block_bwd_dkdv_kernel<D>, dim3((unsigned)(p.max_n_kb * p.n_blk * p.kv_cols)),
-                       dim3(kThreadsKv), 0, stream, p);
+hipError_t launch_dkdv(BwdParams p, hipStream_t stream) {
+    const int64_t items = p.max_n_kb * p.n_blk * p.kv_cols;
+    // one 8-wave block per CU: eight rounds are 2048 blocks (at four, the 8K share's launch
+    // of 1024 blocks lost 7% to the spare blocks and claims)
+    const int64_t grid = use_queues(p, items, p.kv_xcd_cols, 2048, stream);
+    hipLaunchKernelGGL(block_bwd_dkdv_kernel<D>, dim3((unsigned)grid), dim3(kThreadsKv), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -877,6 +974,9 @@ BwdParams block_params(const BlockBwdArgs& a) {
     p.n_blk = 1;
     p.max_n_kb = p.n_kb;
     p.kv[0] = BwdKV{p.k, p.v, p.kvpos, p.dk, p.dv, p.seq_kv, p.n_kb};
+    p.n_queues = 1;  // set by each launch
+    p.slot = 0;
+    p.per_q = 0;
     return p;
 }
 

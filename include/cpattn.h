@@ -26,16 +26,17 @@
  * - Sizes are int64 and address arithmetic is 64-bit (tensors above 2^31 elements are
  *   supported), except a lane's offset within one tile of up to 128 rows, which the bf16
  *   kernels form in 32 bits: their calls bound a row at 2^24 elements.
- * - The library keeps no state between calls except a small array of work counters in
- *   device memory (16 KB per device, part of the loaded code, never allocated): a bf16
- *   attention launch of at least 1024 workgroups (cpattn_block_fwd and the calls built on
- *   it) lets its workgroups take query tiles from queues counted there, so that the chip's
- *   XCDs, which hold different clocks under load, end together.  Successive calls take the
- *   array's 256 slots in turn, and a kernel on the call's stream zeroes the slot first (no
- *   memset, so such a call can be captured in a graph).  Results do not depend on which
- *   workgroup takes which tile.  Calls on different streams may run concurrently as long
- *   as their buffers do not overlap and fewer than 256 such launches are in flight on one
- *   device at a time (a slot reused by a launch still running would be shared).
+ * - The library keeps no state between calls except small arrays of work counters in
+ *   device memory (32 KB per device, part of the loaded code, never allocated).  A long
+ *   bf16 launch lets its workgroups take their work from queues counted there, so that
+ *   the chip's XCDs, which hold different clocks under load, end together: a forward of
+ *   at least 1024 workgroups, a backward dq launch of at least 4096, a dk/dv launch of at
+ *   least 2048.  Successive launches take the arrays' 256 slots in turn, and a kernel on
+ *   the call's stream zeroes the slot first (no memset, so such a call can be captured in
+ *   a graph).  Results do not depend on which workgroup takes which item.  Calls on
+ *   different streams may run concurrently as long as their buffers do not overlap and
+ *   fewer than 256 such launches are in flight on one device at a time (a slot reused by
+ *   a launch still running would be shared).
  */
 #ifndef CPATTN_H
 #define CPATTN_H

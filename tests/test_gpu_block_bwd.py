@@ -259,6 +259,10 @@ def _ring_bwd_check(w, rows_per_chunk, key_samples, exact_forward):
     ("bf16", 3, 70, 8, 8, 64, 2, 2),     # head dim 64, batch 2, the last rank
     ("bf16", 8, 256, 32, 8, 128, 1, 3),  # whole tiles, the long share's head layout
     ("fp32", 2, 33, 4, 2, 64, 1, 0),
+    # 16384 local rows: the dq launches (4096 blocks) and the one dk/dv launch (4096 blocks)
+    # take their work from queues across the XCDs, the per-step dk/dv launches (1024 blocks)
+    # do not, so this also pins the queue order's bits to the static order's
+    ("bf16", 4, 8192, 32, 8, 128, 1, 3),
 ])
 def test_ring_share_bwd_single_equals_steps(dtype, C, t, Hq, Hkv, D, B, rank):
     """The share's backward in one call (cpattn_ring_share_bwd: dq per step, dk and dv of all
